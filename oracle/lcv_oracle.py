@@ -1,0 +1,224 @@
+"""Plain fp64 CPU oracle of LongCat-Video block-sparse 3D self-attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run this
+module: only the test-suite, the smoke check of the graft entry point and the
+``cpu_baseline`` leg of the benchmark use it.  It shares no code with the HIP path
+(only the seeded input generator in ``lcv_inputs`` feeds both).
+
+What it computes is the plain definition of the method, written out with no blocking,
+fusion or reordering beyond what that definition states:
+
+* token -> (t, y, x) map of the patchified latent grid, row-major in t, y, x;
+* partitioned 3D-RoPE: channels [0,16) rotate with t, [16,40) with y, [40,64) with x,
+  interleaved channel pairs treated as complex numbers, pair p of a section of width
+  d rotating by pos * theta**(-2p/d)  [longcat-video-rs page, section 03 "Partitioned
+  3D-RoPE (16T+24H+24W)"; myzaker article, section on technical principles: 3D RoPE
+  on visual tokens];
+* block mask over 64-token blocks: query block i sees key block j iff |i-j| <= local
+  (sliding window) or j is a multiple of the global stride  [longcat-video-rs page,
+  section 02 benchmark table "block=64, local=2, stride=4" and section 03
+  "Block-Sparse & Multi-Audio": local sliding-window blocks plus strided global
+  key/value blocks; zhichai.net post, section "Block Sparse Attention": dense inside
+  a block, sparse between blocks];
+* condition isolation at token level: a condition query (q < C) sees only condition
+  keys (k < C)  [myzaker article, section on technical principles: block attention
+  with a KV cache keeps condition tokens unaffected by noise tokens];
+* softmax attention with scale 1/sqrt(64) and the natural-log LSE of the scaled scores;
+* the CSR of attended key blocks per query block.
+
+Readings taken where the pages are silent (each listed in the design notes): local is
+a radius; global blocks are key columns j % s == 0 (s == 0 disables them); blocks are
+64 consecutive tokens of the flattened (t, y, x) order; condition tokens are the first
+C tokens; noise rows attend by the layout alone; RoPE pairs are adjacent channels,
+integer positions from 0, theta = 1e4; attention is bidirectional; a row with no
+attended key yields out = 0 and lse = -inf.
+
+Every function is pinned by the CPU tests (tests/test_oracle_*.py) to properties fixed
+by the pages or by mathematics; nothing here is unpinned.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+HEAD_DIM = 64
+BLOCK = 64
+# (first channel, section width, axis) with axis 0 = t, 1 = y, 2 = x.
+ROPE_SECTIONS = ((0, 16, 0), (16, 24, 1), (40, 24, 2))
+SOFTMAX_SCALE = 1.0 / math.sqrt(HEAD_DIM)
+
+
+# --------------------------------------------------------------------------- grid
+def token_coords(token_index: np.ndarray, grid) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Flattened token index -> (t, y, x) of a row-major (T, H, W) latent grid."""
+    _, h, w = grid
+    n = np.asarray(token_index, dtype=np.int64)
+    return n // (h * w), (n // w) % h, n % w
+
+
+# --------------------------------------------------------------------------- RoPE
+def rope3d(x: np.ndarray, grid, theta: float = 10000.0, token_offset: int = 0) -> np.ndarray:
+    """Rotate x[..., N, 64] (float64) by the partitioned 3D-RoPE of tokens
+    token_offset .. token_offset+N-1."""
+    n_tokens = np.shape(x)[-2]
+    return rope3d_at(x, np.arange(n_tokens) + token_offset, grid, theta)
+
+
+def rope3d_at(x: np.ndarray, tokens: np.ndarray, grid, theta: float = 10000.0) -> np.ndarray:
+    """Rotate the rows x[..., R, 64] that sit at token indices ``tokens`` [R]."""
+    x = np.asarray(x, dtype=np.float64)
+    coords = token_coords(tokens, grid)
+    out = x.copy()
+    for c0, width, axis in ROPE_SECTIONS:
+        pos = coords[axis].astype(np.float64)
+        for p in range(width // 2):
+            phi = pos * theta ** (-2.0 * p / width)
+            cos, sin = np.cos(phi), np.sin(phi)
+            a = x[..., c0 + 2 * p]
+            b = x[..., c0 + 2 * p + 1]
+            out[..., c0 + 2 * p] = a * cos - b * sin
+            out[..., c0 + 2 * p + 1] = a * sin + b * cos
+    return out
+
+
+# --------------------------------------------------------------------------- layout
+def n_blocks_of(n_tokens: int) -> int:
+    return -(-n_tokens // BLOCK)
+
+
+def block_mask(n_blocks: int, local: int, stride: int) -> np.ndarray:
+    """Mb[i, j] = |i - j| <= local  or  (stride >= 1 and j % stride == 0)."""
+    i = np.arange(n_blocks)[:, None]
+    j = np.arange(n_blocks)[None, :]
+    mb = np.abs(i - j) <= local
+    if stride >= 1:
+        mb = mb | (j % stride == 0)
+    return mb
+
+
+def token_mask_rows(rows: np.ndarray, n_tokens: int, cond_len: int, local: int, stride: int) -> np.ndarray:
+    """M[q, k] for the query tokens in ``rows`` and every key k < N:
+    the block mask of (q // 64, k // 64) and the condition rule (q >= C or k < C)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.arange(n_tokens, dtype=np.int64)
+    qi = rows // BLOCK
+    kj = keys // BLOCK
+    i = qi[:, None]
+    j = kj[None, :]
+    mb = np.abs(i - j) <= local
+    if stride >= 1:
+        mb = mb | (j % stride == 0)
+    cond_ok = (rows[:, None] >= cond_len) | (keys[None, :] < cond_len)
+    return mb & cond_ok
+
+
+def block_pairs_attended(n_tokens: int, cond_len: int, local: int, stride: int) -> np.ndarray:
+    """Block pairs of the block mask that hold at least one attended token pair.
+
+    For non-empty token sets Qi, Kj:  exists q in Qi, k in Kj with (q >= C or k < C)
+    holds iff (some q in Qi has q >= C) or (some k in Kj has k < C)."""
+    n = n_blocks_of(n_tokens)
+    mb = block_mask(n, local, stride)
+    last_row = np.minimum(np.arange(n) * BLOCK + BLOCK, n_tokens) - 1
+    first_key = np.arange(n) * BLOCK
+    has_noise_row = last_row >= cond_len
+    has_cond_key = first_key < cond_len
+    return mb & (has_noise_row[:, None] | has_cond_key[None, :])
+
+
+def csr(n_tokens: int, cond_len: int, local: int, stride: int) -> tuple[np.ndarray, np.ndarray]:
+    """row_ptr[n+1], col_idx[nnz] (int32): ascending attended key blocks per query block."""
+    pairs = block_pairs_attended(n_tokens, cond_len, local, stride)
+    counts = pairs.sum(axis=1)
+    row_ptr = np.zeros(pairs.shape[0] + 1, dtype=np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    col_idx = np.nonzero(pairs)[1]          # row-major order -> ascending j per row
+    return row_ptr.astype(np.int32), col_idx.astype(np.int32)
+
+
+def attended_pairs(n_tokens: int, cond_len: int, local: int, stride: int) -> int:
+    """Number of (q, k) token pairs with M[q, k] = 1, summed over block pairs of the mask:
+    noise rows see every key of the block, condition rows only its condition keys."""
+    n = n_blocks_of(n_tokens)
+    mb = block_mask(n, local, stride)
+    lo = np.arange(n) * BLOCK
+    hi = np.minimum(lo + BLOCK, n_tokens)
+    size = hi - lo
+    n_cond = np.clip(cond_len - lo, 0, size)          # tokens < C in each block
+    n_noise = size - n_cond
+    per_pair = n_noise[:, None] * size[None, :] + n_cond[:, None] * n_cond[None, :]
+    return int((per_pair * mb).sum())
+
+
+# --------------------------------------------------------------------------- attention
+def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray):
+    """Softmax attention of q[R,64] over k, v[N,64] with boolean mask[R,N] (fp64).
+    Returns out[R,64] and the natural-log LSE[R] of the scaled scores.  Rows whose
+    mask is empty give out = 0 and lse = -inf."""
+    s = (q @ k.T) * SOFTMAX_SCALE
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    out = (e @ v) / l_safe[:, None]
+    out[empty] = 0.0
+    lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    return out, lse
+
+
+def bsa_forward(q, k, v, grid, cond_len: int, local: int, stride: int, theta: float = 10000.0,
+                rope_q: bool = True, rope_k: bool = True, rows=None):
+    """Block-sparse 3D self-attention of q, k, v [B, H, N, 64] (float64).
+
+    rows: optional query token indices to evaluate (all rows if None).
+    Returns out [B, H, R, 64] and lse [B, H, R]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    bsz, heads, n_tokens, _ = q.shape
+    rows = np.arange(n_tokens) if rows is None else np.asarray(rows, dtype=np.int64)
+    mask = token_mask_rows(rows, n_tokens, cond_len, local, stride)
+    out = np.zeros((bsz, heads, rows.size, HEAD_DIM))
+    lse = np.zeros((bsz, heads, rows.size))
+    for b in range(bsz):
+        for h in range(heads):
+            qb = q[b, h, rows]
+            kb = k[b, h]
+            if rope_q:
+                qb = rope3d_at(qb, rows, grid, theta)
+            if rope_k:
+                kb = rope3d(kb, grid, theta)
+            out[b, h], lse[b, h] = masked_attention(qb, kb, v[b, h], mask)
+    return out, lse
+
+
+def bsa_forward_cached(q_noise, k_noise, v_noise, k_cond, v_cond, grid, cond_len: int, local: int,
+                       stride: int, theta: float = 10000.0, rope_q: bool = True, rope_k: bool = True,
+                       rows=None):
+    """Noise-token rows [C, N) of the block-sparse attention whose key/value sequence is
+    the cached condition K/V followed by the noise K/V.  q_noise, k_noise, v_noise are
+    [B, H, N-C, 64]; k_cond, v_cond are [B, H, C, 64].  ``rows`` (optional) are indices
+    into the noise rows.  Returns out [B, H, R, 64] and lse [B, H, R]."""
+    q_noise = np.asarray(q_noise, dtype=np.float64)
+    k_full = np.concatenate([np.asarray(k_cond, np.float64), np.asarray(k_noise, np.float64)], axis=2)
+    v_full = np.concatenate([np.asarray(v_cond, np.float64), np.asarray(v_noise, np.float64)], axis=2)
+    bsz, heads, n_tokens, _ = k_full.shape
+    local_rows = np.arange(n_tokens - cond_len) if rows is None else np.asarray(rows, dtype=np.int64)
+    tokens = local_rows + cond_len
+    mask = token_mask_rows(tokens, n_tokens, cond_len, local, stride)
+    out = np.zeros((bsz, heads, local_rows.size, HEAD_DIM))
+    lse = np.zeros((bsz, heads, local_rows.size))
+    for b in range(bsz):
+        for h in range(heads):
+            qb = q_noise[b, h, local_rows]
+            kb = k_full[b, h]
+            if rope_q:
+                qb = rope3d_at(qb, tokens, grid, theta)
+            if rope_k:
+                kb = rope3d(kb, grid, theta)
+            out[b, h], lse[b, h] = masked_attention(qb, kb, v_full[b, h], mask)
+    return out, lse

@@ -1,0 +1,350 @@
+"""Pins of the fp64 oracle: checks against facts fixed by the pages or by mathematics.
+
+Each ``pin_*`` function takes an oracle implementation (the real ``oracle`` package or a
+copy with a planted mistake) and raises AssertionError when the implementation breaks
+the fact it pins.  None of them re-types the oracle's own formula: each uses a second,
+independent formulation (complex arithmetic, brute-force loops with math.fsum, a
+library routine, a hand-derived fixture or a closed form).
+"""
+from __future__ import annotations
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ----------------------------------------------------------------------------- RoPE
+def pin_rope_norm(impl):
+    """Rotations conserve the norm of every token (longcat-video-rs page, section 01
+    studio readout "3D-RoPE norm conservation 1.00000"); fp64 holds it to 1e-12."""
+    rng = np.random.default_rng(11)
+    grid = (6, 9, 13)
+    x = rng.standard_normal((3, 6 * 9 * 13, 64))
+    y = impl.rope3d(x, grid)
+    nx = np.linalg.norm(x, axis=-1)
+    ny = np.linalg.norm(y, axis=-1)
+    assert np.max(np.abs(ny / nx - 1.0)) < 1e-12
+    # every adjacent channel pair is a rotation on its own: pair norms are conserved
+    px = np.hypot(x[..., 0::2], x[..., 1::2])
+    py = np.hypot(y[..., 0::2], y[..., 1::2])
+    assert np.max(np.abs(px - py)) < 1e-12
+
+
+def pin_rope_origin_identity(impl):
+    """The token at (t, y, x) = (0, 0, 0) is left unchanged."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((1, 64))
+    y = impl.rope3d(x, (4, 5, 6), token_offset=0)
+    assert np.array_equal(x, y)
+
+
+def _textbook_rope_1d(z: np.ndarray, pos: np.ndarray, dim: int, theta: float) -> np.ndarray:
+    """Textbook rotary embedding of complex pairs z[..., dim/2] at integer positions:
+    z_p * exp(i * pos * theta**(-2p/dim)), frequencies written as 1/theta**(arange(0,dim,2)/dim)."""
+    inv_freq = 1.0 / theta ** (np.arange(0, dim, 2, dtype=np.float64) / dim)
+    return z * np.exp(1j * np.outer(pos, inv_freq))
+
+
+def pin_rope_sections_textbook(impl):
+    """Each of the three sections is a textbook 1-D RoPE of its own axis: channels
+    [0,16) follow t, [16,40) follow y, [40,64) follow x (longcat-video-rs page,
+    section 03 "Partitioned 3D-RoPE (16T+24H+24W)"), with adjacent channels as the
+    real and imaginary parts of one complex number."""
+    rng = np.random.default_rng(13)
+    grid = (5, 7, 11)
+    theta = 10000.0
+    n = grid[0] * grid[1] * grid[2]
+    x = rng.standard_normal((n, 64))
+    y = impl.rope3d(x, grid, theta)
+    t, yy, xx = np.unravel_index(np.arange(n), grid)
+    z = x[:, 0::2] + 1j * x[:, 1::2]
+    ref = np.concatenate([
+        _textbook_rope_1d(z[:, 0:8], t, 16, theta),
+        _textbook_rope_1d(z[:, 8:20], yy, 24, theta),
+        _textbook_rope_1d(z[:, 20:32], xx, 24, theta),
+    ], axis=1)
+    got = y[:, 0::2] + 1j * y[:, 1::2]
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def pin_rope_relative_position(impl):
+    """<R(a) q, R(b) k> depends on a - b only: shifting both tokens by the same
+    (dt, dy, dx) leaves the inner product unchanged (composition of rotations)."""
+    rng = np.random.default_rng(14)
+    grid = (9, 9, 9)
+    q = rng.standard_normal((1, 64))
+    k = rng.standard_normal((1, 64))
+
+    def tok(t, y, x):
+        return int(np.ravel_multi_index((t, y, x), grid))
+
+    def dot(a, b):
+        qa = impl.rope3d(q, grid, token_offset=a)
+        kb = impl.rope3d(k, grid, token_offset=b)
+        return float((qa * kb).sum())
+
+    base = dot(tok(1, 2, 3), tok(4, 1, 0))
+    for shift in ((2, 0, 0), (0, 3, 0), (0, 0, 5), (3, 4, 2)):
+        a = tok(1 + shift[0], 2 + shift[1], 3 + shift[2])
+        b = tok(4 + shift[0], 1 + shift[1], 0 + shift[2])
+        assert abs(dot(a, b) - base) < 1e-11 * max(1.0, abs(base))
+
+
+def pin_rope_closed_form_first_pair(impl):
+    """Pair 0 of each section turns by exactly its axis position in radians
+    (theta**0 = 1): the unit vector (1, 0) at position p maps to (cos p, sin p)."""
+    grid = (8, 8, 8)
+    for c0, axis in ((0, 0), (16, 1), (40, 2)):
+        pos = [0, 0, 0]
+        pos[axis] = 3
+        x = np.zeros((1, 64))
+        x[0, c0] = 1.0
+        y = impl.rope3d(x, grid, token_offset=int(np.ravel_multi_index(pos, grid)))
+        assert abs(y[0, c0] - math.cos(3.0)) < 1e-15 and abs(y[0, c0 + 1] - math.sin(3.0)) < 1e-15
+
+
+# ----------------------------------------------------------------------------- layout
+def _brute_token_mask(n_tokens, cond_len, local, stride):
+    """Token mask by pure-Python loops over every (q, k)."""
+    m = np.zeros((n_tokens, n_tokens), dtype=bool)
+    for q in range(n_tokens):
+        for k in range(n_tokens):
+            i, j = q // 64, k // 64
+            in_layout = abs(i - j) <= local or (stride >= 1 and j % stride == 0)
+            m[q, k] = in_layout and (q >= cond_len or k < cond_len)
+    return m
+
+
+LAYOUT_CASES = [
+    # (N, C, local, stride)
+    (128, 0, 0, 0), (128, 0, 0, 2), (128, 37, 0, 2), (200, 0, 1, 3), (200, 64, 0, 4),
+    (256, 100, 2, 4), (330, 130, 1, 2), (330, 330, 0, 3), (448, 65, 2, 0), (448, 1, 0, 1),
+    (512, 0, 2, 4), (200, 63, 0, 3), (330, 329, 1, 4), (130, 127, 0, 2),
+]
+
+
+def pin_token_mask_brute_force(impl):
+    """The token mask and the CSR equal brute-force enumeration of the rule on small
+    inputs, including ragged N and condition lengths that split a block."""
+    for n_tokens, cond, local, stride in LAYOUT_CASES:
+        ref = _brute_token_mask(n_tokens, cond, local, stride)
+        got = impl.token_mask_rows(np.arange(n_tokens), n_tokens, cond, local, stride)
+        assert np.array_equal(got, ref), (n_tokens, cond, local, stride)
+        n = -(-n_tokens // 64)
+        blocks = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            for j in range(n):
+                blocks[i, j] = ref[64 * i:64 * i + 64, 64 * j:64 * j + 64].any()
+        row_ptr, col_idx = impl.csr(n_tokens, cond, local, stride)
+        exp_ptr = [0]
+        exp_col = []
+        for i in range(n):
+            cols = [j for j in range(n) if blocks[i, j]]
+            exp_col += cols
+            exp_ptr.append(len(exp_col))
+        assert row_ptr.tolist() == exp_ptr and col_idx.tolist() == exp_col, (n_tokens, cond, local, stride)
+        assert impl.attended_pairs(n_tokens, cond, local, stride) == int(ref.sum())
+
+
+def pin_tiny_csr_golden(impl):
+    """Hand-derived CSR of the 512-token, local 2, stride 4 layout (tests/golden)."""
+    g = json.loads((GOLDEN / "tiny_csr.json").read_text())
+    row_ptr, col_idx = impl.csr(g["n_tokens"], g["cond_len"], g["local_blocks"], g["global_stride"])
+    assert row_ptr.tolist() == g["row_ptr"]
+    assert col_idx.tolist() == [j for row in g["rows"] for j in row]
+
+
+def pin_two_block_layouts(impl):
+    """Two-block (N = 128) layouts over local in {0,1,2} and stride in {0,1,2},
+    enumerated by hand: rows of attended key blocks."""
+    expected = {
+        (0, 0): [[0], [1]],
+        (0, 1): [[0, 1], [0, 1]],
+        (0, 2): [[0], [0, 1]],
+    }
+    for local in (0, 1, 2):
+        for stride in (0, 1, 2):
+            rows = expected.get((local, stride), [[0, 1], [0, 1]])
+            row_ptr, col_idx = impl.csr(128, 0, local, stride)
+            got = [col_idx[row_ptr[i]:row_ptr[i + 1]].tolist() for i in range(2)]
+            assert got == rows, (local, stride, got)
+
+
+def _nnz_closed_form(n_tokens, cond_len, local, stride):
+    """Sum over query blocks of |band u multiples of s|, limited to key blocks that hold a
+    condition key when every row of the query block is a condition row:
+    |band| + ceil(lim/s) - #(multiples of s inside the band)."""
+    n = -(-n_tokens // 64)
+    jc = -(-cond_len // 64)          # key blocks holding at least one condition key
+    total = 0
+    for i in range(n):
+        last_row = min(64 * i + 63, n_tokens - 1)
+        lim = n if last_row >= cond_len else jc
+        lo, hi = max(0, i - local), min(i + local, lim - 1)
+        band = hi - lo + 1 if hi >= lo else 0
+        if stride >= 1:
+            mult_all = -(-lim // stride)
+            mult_band = (hi // stride - (lo - 1) // stride) if band else 0
+        else:
+            mult_all = mult_band = 0
+        total += band + mult_all - mult_band
+    return total
+
+
+CONFIG_LAYOUTS = [
+    # (N, C) of the five workloads, layout (local, stride)
+    (512, 0, 2, 4), (37440, 0, 2, 4), (37440, 1560, 2, 4), (86400, 0, 2, 4), (62400, 24960, 2, 4),
+    (62400, 24960, 64, 3), (62400, 24960, 2, 3), (62400, 24960, 2, 8), (62400, 24960, 2, 12),
+    (62400, 24960, 2, 16), (1000, 333, 3, 5),
+]
+
+
+def pin_nnz_closed_form(impl):
+    """nnz of the CSR equals the closed form on every workload and density-sweep point."""
+    for n_tokens, cond, local, stride in CONFIG_LAYOUTS:
+        row_ptr, col_idx = impl.csr(n_tokens, cond, local, stride)
+        assert int(row_ptr[-1]) == col_idx.size == _nnz_closed_form(n_tokens, cond, local, stride)
+
+
+def pin_attended_pairs_closed_form(impl):
+    """Attended pairs without condition tokens on a block-aligned N: nnz * 64 * 64."""
+    for n_tokens, local, stride in ((37440, 2, 4), (86400, 2, 4), (62400, 2, 12)):
+        assert impl.attended_pairs(n_tokens, 0, local, stride) == 4096 * _nnz_closed_form(n_tokens, 0, local, stride)
+
+
+# ----------------------------------------------------------------------------- attention
+def _brute_attention_row(qrow, keys, vals, allowed):
+    """One row by pure-Python loops and math.fsum (fp64)."""
+    scores = []
+    for k in range(len(keys)):
+        if allowed[k]:
+            scores.append((k, math.fsum(qrow[d] * keys[k][d] for d in range(64)) / 8.0))
+    if not scores:
+        return [0.0] * 64, -math.inf
+    m = max(s for _, s in scores)
+    w = [(k, math.exp(s - m)) for k, s in scores]
+    l = math.fsum(e for _, e in w)
+    out = [math.fsum(e * vals[k][d] for k, e in w) / l for d in range(64)]
+    return out, m + math.log(l)
+
+
+def pin_two_block_brute_force(impl):
+    """Two-block inputs (N = 128, local 0, strides 0 and 2) against a pure-Python
+    attention with math.fsum, for condition lengths {0, 1, 37, 64, 100, 128}."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, 1, 128, 64))
+    k = rng.standard_normal((1, 1, 128, 64))
+    v = rng.standard_normal((1, 1, 128, 64))
+    grid = (2, 4, 16)
+    for stride in (0, 2):
+        for cond in (0, 1, 37, 64, 100, 128):
+            out, lse = impl.bsa_forward(q, k, v, grid, cond, 0, stride, rope_q=False, rope_k=False)
+            for r in range(128):
+                allowed = [(abs(r // 64 - c // 64) <= 0 or (stride and (c // 64) % stride == 0))
+                           and (r >= cond or c < cond) for c in range(128)]
+                ro, rl = _brute_attention_row(q[0, 0, r].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), allowed)
+                assert np.max(np.abs(out[0, 0, r] - ro)) < 1e-12, (stride, cond, r)
+                assert abs(lse[0, 0, r] - rl) < 1e-12, (stride, cond, r)
+
+
+def pin_full_layout_is_dense_sdpa(impl):
+    """With a layout that keeps every block pair (stride 1) and no condition tokens the
+    method is plain softmax attention: compare with torch's scaled_dot_product_attention
+    and logsumexp in float64 on the CPU."""
+    import torch
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((2, 3, 300, 64))
+    k = rng.standard_normal((2, 3, 300, 64))
+    v = rng.standard_normal((2, 3, 300, 64))
+    for local, stride in ((0, 1), (10, 0)):
+        out, lse = impl.bsa_forward(q, k, v, (3, 10, 10), 0, local, stride, rope_q=False, rope_k=False)
+        tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+        ref_lse = torch.logsumexp(tq @ tk.transpose(-1, -2) / 8.0, dim=-1).numpy()
+        assert np.max(np.abs(out - ref)) < 1e-12
+        assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
+def pin_condition_isolation(impl):
+    """Condition queries never see noise tokens (myzaker article, technical principles):
+    replacing every noise Q/K/V leaves condition rows of out and lse bitwise unchanged."""
+    rng = np.random.default_rng(23)
+    grid = (4, 5, 13)            # 260 tokens, condition = first 1.5 frames = 97 tokens
+    n = 260
+    cond = 97
+    q, k, v = (rng.standard_normal((1, 2, n, 64)) for _ in range(3))
+    out1, lse1 = impl.bsa_forward(q, k, v, grid, cond, 1, 2)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for a in (q2, k2, v2):
+        a[:, :, cond:] = rng.standard_normal(a[:, :, cond:].shape) * 3.0
+    out2, lse2 = impl.bsa_forward(q2, k2, v2, grid, cond, 1, 2)
+    assert np.array_equal(out1[:, :, :cond], out2[:, :, :cond])
+    assert np.array_equal(lse1[:, :, :cond], lse2[:, :, :cond])
+    assert not np.array_equal(out1[:, :, cond:], out2[:, :, cond:])
+
+
+def pin_cached_equals_full(impl):
+    """The cached call (condition K/V from the cache, noise rows only) equals rows [C, N)
+    of the full call on the concatenated sequence."""
+    rng = np.random.default_rng(24)
+    grid = (3, 6, 20)
+    n = 360
+    for cond in (0, 120, 150):
+        q, k, v = (rng.standard_normal((1, 2, n, 64)) for _ in range(3))
+        full_o, full_l = impl.bsa_forward(q, k, v, grid, cond, 1, 3)
+        o, l = impl.bsa_forward_cached(q[:, :, cond:], k[:, :, cond:], v[:, :, cond:], k[:, :, :cond],
+                                       v[:, :, :cond], grid, cond, 1, 3)
+        assert np.max(np.abs(o - full_o[:, :, cond:])) < 1e-13
+        assert np.max(np.abs(l - full_l[:, :, cond:])) < 1e-13
+
+
+def pin_rope_shift_invariance(impl):
+    """Shifting every token's time position by the same amount leaves the attention
+    output unchanged (RoPE scores depend on relative positions only)."""
+    rng = np.random.default_rng(25)
+    grid = (4, 6, 10)
+    n = 240
+    q, k, v = (rng.standard_normal((1, 1, n, 64)) for _ in range(3))
+    out, _ = impl.bsa_forward(q, k, v, grid, 0, 1, 2)
+    shift = 3 * 6 * 10      # three frames later
+    qs = impl.rope3d(q, grid, token_offset=shift)
+    ks = impl.rope3d(k, grid, token_offset=shift)
+    out_s, _ = impl.bsa_forward(qs, ks, v, grid, 0, 1, 2, rope_q=False, rope_k=False)
+    assert np.max(np.abs(out - out_s)) < 1e-12
+
+
+def pin_sampled_rows_match_full(impl):
+    """Evaluating a subset of rows gives the same values as the full evaluation."""
+    rng = np.random.default_rng(26)
+    grid = (3, 8, 12)
+    n = 288
+    q, k, v = (rng.standard_normal((1, 2, n, 64)) for _ in range(3))
+    rows = np.array([0, 5, 63, 64, 100, 200, 287])
+    out, lse = impl.bsa_forward(q, k, v, grid, 70, 2, 4)
+    out_r, lse_r = impl.bsa_forward(q, k, v, grid, 70, 2, 4, rows=rows)
+    assert np.max(np.abs(out[:, :, rows] - out_r)) < 1e-13
+    assert np.max(np.abs(lse[:, :, rows] - lse_r)) < 1e-13
+
+
+def pin_empty_row(impl):
+    """A row with no attended key gives out = 0 and lse = -inf."""
+    q = np.ones((2, 64))
+    k = np.ones((3, 64))
+    v = np.ones((3, 64))
+    mask = np.array([[False, False, False], [True, False, False]])
+    out, lse = impl.masked_attention(q, k, v, mask)
+    assert np.all(out[0] == 0.0) and lse[0] == -np.inf
+    assert np.allclose(out[1], 1.0) and abs(lse[1] - 8.0) < 1e-12
+
+
+ALL_PINS = [
+    pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
+    pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
+    pin_two_block_layouts, pin_nnz_closed_form, pin_attended_pairs_closed_form,
+    pin_two_block_brute_force, pin_full_layout_is_dense_sdpa, pin_condition_isolation,
+    pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_empty_row,
+]

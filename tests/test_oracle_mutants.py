@@ -1,0 +1,67 @@
+"""Planted mistakes: a copy of the oracle with one plausible error must fail a pin.
+
+Each mutant edits the oracle's source text on the CPU, loads it as a separate module
+and runs every pin; the test passes when at least one pin rejects the mutant.  This
+shows the pins constrain every part of the oracle (a dropped term, a wrong sign or
+index, a transposed operand)."""
+import types
+from pathlib import Path
+
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+SRC = (Path(__file__).resolve().parent.parent / "oracle" / "lcv_oracle.py").read_text()
+
+MUTANTS = {
+    "rope_sign": [("out[..., c0 + 2 * p] = a * cos - b * sin", "out[..., c0 + 2 * p] = a * cos + b * sin")],
+    "rope_rotate_half_pairing": [("b = x[..., c0 + 2 * p + 1]", "b = x[..., c0 + p + width // 2]"),
+                                 ("out[..., c0 + 2 * p + 1] = a * sin + b * cos",
+                                  "out[..., c0 + p + width // 2] = a * sin + b * cos"),
+                                 ("a = x[..., c0 + 2 * p]", "a = x[..., c0 + p]"),
+                                 ("out[..., c0 + 2 * p] = a * cos - b * sin", "out[..., c0 + p] = a * cos - b * sin")],
+    "rope_freq_exponent": [("theta ** (-2.0 * p / width)", "theta ** (-1.0 * p / width)")],
+    "rope_axes_swapped": [("((0, 16, 0), (16, 24, 1), (40, 24, 2))", "((0, 16, 0), (16, 24, 2), (40, 24, 1))")],
+    "rope_section_bounds": [("((0, 16, 0), (16, 24, 1), (40, 24, 2))", "((0, 16, 0), (16, 16, 1), (32, 32, 2))")],
+    "coords_row_major_swapped": [("return n // (h * w), (n // w) % h, n % w", "return n // (h * w), (n // h) % w, n % h")],
+    "window_strict": [("mb = np.abs(i - j) <= local", "mb = np.abs(i - j) < local")],
+    "global_offset": [("mb = mb | (j % stride == 0)", "mb = mb | (j % stride == stride - 1)")],
+    "global_rows_not_cols": [("mb = mb | (j % stride == 0)", "mb = mb | (i % stride == 0)")],
+    "condition_reversed": [("cond_ok = (rows[:, None] >= cond_len) | (keys[None, :] < cond_len)",
+                            "cond_ok = (rows[:, None] < cond_len) | (keys[None, :] >= cond_len)")],
+    "condition_dropped": [("return mb & cond_ok", "return mb")],
+    "block_pair_noise_test": [("has_noise_row = last_row >= cond_len", "has_noise_row = last_row > cond_len")],
+    "softmax_scale": [("SOFTMAX_SCALE = 1.0 / math.sqrt(HEAD_DIM)", "SOFTMAX_SCALE = 1.0 / HEAD_DIM")],
+    "lse_base2": [("lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))",
+                   "lse = np.where(empty, -np.inf, m_safe + np.log2(l_safe))")],
+    "lse_missing_max": [("lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))",
+                         "lse = np.where(empty, -np.inf, np.log(l_safe))")],
+    "scores_use_v": [("s = (q @ k.T) * SOFTMAX_SCALE", "s = (q @ v.T) * SOFTMAX_SCALE")],
+    "no_normalisation": [("out = (e @ v) / l_safe[:, None]", "out = (e @ v)")],
+    "pairs_count_cond": [("n_cond[:, None] * n_cond[None, :]", "n_cond[:, None] * size[None, :]")],
+    "cached_kv_order": [("k_full = np.concatenate([np.asarray(k_cond, np.float64), np.asarray(k_noise, np.float64)], axis=2)",
+                         "k_full = np.concatenate([np.asarray(k_noise, np.float64), np.asarray(k_cond, np.float64)], axis=2)")],
+    "cached_q_positions": [("tokens = local_rows + cond_len", "tokens = local_rows")],
+}
+
+
+def _load_mutant(name):
+    src = SRC
+    for old, new in MUTANTS[name]:
+        assert old in src, f"mutation anchor not found: {old}"
+        src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src, f"oracle_mutant_{name}", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(name)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin rejects the planted mistake {name}"
