@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of LongCat-Video block-sparse 3D self-attention on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input: the attention
+forward with the 3D-RoPE fused into its Q/K loads, over the prebuilt block layout (the
+layout is built once per shape and reused; its build time is reported separately).
+The default workload is T2V 720x1280, 93 frames: latent 24x45x80 = 86,400 tokens,
+32 heads of 64 channels, bf16, local window 2 + global stride 4 blocks.
+
+Prints one JSON line: effective attended TFLOP/s = 4 * 64 * attended token pairs *
+heads / time, the MFMA roofline of the attention kernel and the fp64 oracle timed on the
+host's cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from lcv_inputs import WORKLOADS, bf16_bits_to_f64, workload_inputs  # noqa: E402
+
+METRIC = "effective attended TFLOP/s + % MFMA peak, 720p 93-frame block-sparse attn"
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def traffic_from_profile(path: str | None):
+    """HBM bytes per launch of the attention kernel from a committed counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), if present."""
+    if not path or not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        return float(data["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, seconds: float = 12.0) -> dict:
+    """The fp64 oracle on a bounded sample: one head, as many query rows as fit the
+    time budget (doubling from 256), scaled to effective attended TFLOP/s."""
+    import oracle
+    from lcv_inputs import qkv_bits
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    qb, kb, vb = qkv_bits(w.seed, 1, 1, w.n_tokens)
+    q, k, v = bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+    rng = np.random.default_rng(0)
+    rows_n = 256
+    best = None
+    t_total = 0.0
+    while True:
+        rows = np.sort(rng.choice(w.n_tokens, size=min(rows_n, w.n_tokens), replace=False))
+        t0 = time.perf_counter()
+        oracle.bsa_forward(q, k, v, w.grid, w.cond_len, w.local_blocks, w.global_stride, w.theta, rows=rows)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        mask = oracle.token_mask_rows(rows, w.n_tokens, w.cond_len, w.local_blocks, w.global_stride)
+        flops = 4.0 * 64 * float(mask.sum())
+        best = (rows.size, dt, flops)
+        if t_total >= seconds or rows_n >= w.n_tokens or dt * 2 + t_total > 3 * seconds:
+            break
+        rows_n *= 2
+    n_rows, dt, flops = best
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: 1 of {w.heads} heads, {n_rows} random query rows of {w.n_tokens} "
+                      f"(fp64 numpy oracle: RoPE + masked dense attention), {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t2v720", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-rope", action="store_true", help="inputs pre-rotated (no fused RoPE)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              f"this build has no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_attention_lcv_amd as bsa
+
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: grid {w.grid} N={w.n_tokens} heads={w.heads} C={w.cond_len}")
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+
+    t0 = time.perf_counter()
+    layout = bsa.build_layout(w.n_tokens, w.local_blocks, w.global_stride, w.cond_len)
+    layout_ms = (time.perf_counter() - t0) * 1e3
+    info = layout.info
+    flops = 4.0 * 64 * info["attended_pairs"] * w.heads * w.batch
+    log(f"[bench] layout nnz={info['nnz']} pairs/head={info['attended_pairs']} build {layout_ms:.2f} ms")
+
+    qb, kb, vb = workload_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    del qb, kb, vb
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device="cuda")
+    grid = None if args.no_rope else w.grid
+
+    def step():
+        bsa.forward(q, k, v, layout, grid=grid, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = float(np.mean(per_launch))
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms "
+        f"(min {min(per_launch):.3f}, max {max(per_launch):.3f}), {value:.1f} TFLOP/s effective")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "grid": list(w.grid), "tokens": w.n_tokens, "heads": w.heads, "head_dim": 64, "batch": w.batch,
+            "cond_len": w.cond_len, "layout": f"block 64, local {w.local_blocks}, stride {w.global_stride}",
+            "rope": "none (pre-rotated)" if args.no_rope else "fused into Q/K loads",
+            "nnz": info["nnz"], "attended_pairs_per_head": info["attended_pairs"],
+            "effective_flops": flops,
+        },
+        "pct_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "layout_build_ms": round(layout_ms, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile(args.traffic_json),
+            "kernel": "bsa_fwd_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    layout.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,248 @@
+"""Python binding of liblcv_bsa: LongCat-Video block-sparse 3D self-attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of the
+C-ABI library (include/lcv_bsa.h).  PyTorch provides device memory and streams.  The
+library must be built (``python -m block_sparse_attention_lcv_amd._build`` or
+``__graft_entry__.build()``); nothing falls back to another implementation when it is
+missing.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "liblcv_bsa.so"
+
+ROPE_Q = 1
+ROPE_K = 2
+
+STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5: "ERR_LAYOUT_MISMATCH",
+                6: "ERR_UNSUPPORTED", 7: "ERR_OOM", 8: "ERR_HIP"}
+
+# Every symbol include/lcv_bsa.h declares.
+EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
+            "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_bsa_forward", "lcv_bsa_forward_cached",
+            "lcv_last_error", "lcv_abi_version")
+
+
+class LayoutParams(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("block", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
+                ("global_stride", ctypes.c_int32), ("cond_len", ctypes.c_int32)]
+
+
+class Rope3dGrid(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("theta", ctypes.c_float)]
+
+
+class LayoutInfo(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
+                ("global_stride", ctypes.c_int32), ("cond_len", ctypes.c_int32), ("max_row_len", ctypes.c_int32),
+                ("nnz", ctypes.c_int64), ("attended_pairs", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class LcvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblcv_bsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m block_sparse_attention_lcv_amd._build")
+    # PyTorch ships its own HIP runtime with the same soname as ROCm's; loading torch first
+    # makes the dynamic linker bind this library to that one runtime instead of a second copy.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(str(LIB_PATH))
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    sig = {
+        "lcv_bsa_layout_query": (i32, [ctypes.POINTER(LayoutParams), ctypes.POINTER(LayoutInfo)]),
+        "lcv_bsa_build_layout": (i32, [ctypes.POINTER(LayoutParams), vp, ctypes.POINTER(vp)]),
+        "lcv_bsa_layout_get_info": (i32, [vp, ctypes.POINTER(LayoutInfo)]),
+        "lcv_bsa_layout_copy_csr": (i32, [vp, vp, vp, vp]),
+        "lcv_bsa_layout_destroy": (None, [vp]),
+        "lcv_rope3d_apply": (i32, [vp, vp, i64, i32, i32, ctypes.POINTER(Rope3dGrid), vp]),
+        "lcv_bsa_forward": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), vp, vp, vp]),
+        "lcv_bsa_forward_cached": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid),
+                                         vp, vp, vp]),
+        "lcv_last_error": (ctypes.c_char_p, []),
+        "lcv_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LcvError(status, lib().lcv_last_error().decode())
+
+
+def _params(n_tokens: int, local_blocks: int, global_stride: int, cond_len: int) -> LayoutParams:
+    return LayoutParams(n_tokens, 64, local_blocks, global_stride, cond_len)
+
+
+def layout_query(n_tokens: int, local_blocks: int = 2, global_stride: int = 4, cond_len: int = 0) -> dict:
+    """Closed-form layout sizes, computed on the host (no GPU needed)."""
+    info = LayoutInfo()
+    _check(lib().lcv_bsa_layout_query(ctypes.byref(_params(n_tokens, local_blocks, global_stride, cond_len)),
+                                      ctypes.byref(info)))
+    return info.as_dict()
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+class Layout:
+    """A built block layout (device CSR + the forward kernel's per-workgroup lists)."""
+
+    def __init__(self, n_tokens: int, local_blocks: int = 2, global_stride: int = 4, cond_len: int = 0, stream=None):
+        handle = ctypes.c_void_p()
+        params = _params(n_tokens, local_blocks, global_stride, cond_len)
+        _check(lib().lcv_bsa_build_layout(ctypes.byref(params), _stream_ptr(stream), ctypes.byref(handle)))
+        self._h = handle
+        info = LayoutInfo()
+        _check(lib().lcv_bsa_layout_get_info(self._h, ctypes.byref(info)))
+        self.info = info.as_dict()
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    @property
+    def n_tokens(self) -> int:
+        return self.info["n_tokens"]
+
+    @property
+    def cond_len(self) -> int:
+        return self.info["cond_len"]
+
+    def csr(self, stream=None):
+        """(row_ptr, col_idx) as int32 device tensors (copies)."""
+        import torch
+        row_ptr = torch.empty(self.info["n_blocks"] + 1, dtype=torch.int32, device="cuda")
+        col_idx = torch.empty(max(self.info["nnz"], 1), dtype=torch.int32, device="cuda")
+        _check(lib().lcv_bsa_layout_copy_csr(self._h, row_ptr.data_ptr(), col_idx.data_ptr(), _stream_ptr(stream)))
+        return row_ptr, col_idx[: self.info["nnz"]]
+
+    def close(self) -> None:
+        if self._h:
+            lib().lcv_bsa_layout_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def build_layout(n_tokens: int, local_blocks: int = 2, global_stride: int = 4, cond_len: int = 0,
+                 stream=None) -> Layout:
+    return Layout(n_tokens, local_blocks, global_stride, cond_len, stream)
+
+
+@dataclass(frozen=True)
+class Grid:
+    T: int
+    H: int
+    W: int
+    theta: float = 10000.0
+
+    def c(self) -> Rope3dGrid:
+        return Rope3dGrid(self.T, self.H, self.W, self.theta)
+
+
+def _as_grid(grid) -> Grid | None:
+    if grid is None or isinstance(grid, Grid):
+        return grid
+    return Grid(*grid)
+
+
+def _bf16(t, name: str):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+    return t.data_ptr()
+
+
+def rope3d_apply(x, grid, token_offset: int = 0, out=None, stream=None):
+    """3D-RoPE of x[..., n_tokens, 64] (bf16); out may be x for in-place use."""
+    import torch
+    g = _as_grid(grid)
+    if x.shape[-1] != 64:
+        raise ValueError("last dimension must be 64")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    n_tokens = x.shape[-2]
+    n_outer = x.numel() // (64 * n_tokens) if n_tokens else 0
+    _check(lib().lcv_rope3d_apply(_bf16(x, "x"), _bf16(y, "out"), n_outer, n_tokens, token_offset,
+                                  ctypes.byref(g.c()), _stream_ptr(stream)))
+    return y
+
+
+def _flags(rope_q: bool, rope_k: bool) -> int:
+    return (ROPE_Q if rope_q else 0) | (ROPE_K if rope_k else 0)
+
+
+def forward(q, k, v, layout: Layout, grid=None, rope_q: bool = True, rope_k: bool = True, out=None, lse=None,
+            with_lse: bool = True, stream=None):
+    """Block-sparse attention of q, k, v [B, H, N, 64] (bf16).  Returns (out, lse)."""
+    import torch
+    B, Hh, N, D = q.shape
+    if D != 64 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share the shape [B, H, N, 64]")
+    g = _as_grid(grid)
+    flags = _flags(rope_q, rope_k) if g is not None else 0
+    out = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    lse_ptr = None if lse is None else lse.data_ptr()
+    _check(lib().lcv_bsa_forward(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), B, Hh, layout.handle,
+                                 layout.cond_len, flags, ctypes.byref(g.c()) if g is not None else None,
+                                 _bf16(out, "out"), lse_ptr, _stream_ptr(stream)))
+    return out, lse
+
+
+def forward_cached(q_noise, k_noise, v_noise, k_cond, v_cond, layout: Layout, grid=None, rope_q: bool = True,
+                   rope_k: bool = True, out=None, lse=None, with_lse: bool = True, stream=None):
+    """Noise rows [C, N) with the condition K/V [B, H, C, 64] taken from a cache."""
+    import torch
+    B, Hh, M, D = q_noise.shape
+    if D != 64 or k_noise.shape != q_noise.shape or v_noise.shape != q_noise.shape:
+        raise ValueError("q_noise, k_noise, v_noise must share the shape [B, H, N-C, 64]")
+    C = layout.cond_len
+    if M != layout.n_tokens - C:
+        raise ValueError(f"noise tensors must hold N-C = {layout.n_tokens - C} tokens")
+    if C > 0 and (k_cond.shape != (B, Hh, C, 64) or v_cond.shape != (B, Hh, C, 64)):
+        raise ValueError("k_cond, v_cond must be [B, H, C, 64]")
+    g = _as_grid(grid)
+    flags = _flags(rope_q, rope_k) if g is not None else 0
+    out = torch.empty_like(q_noise) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, M), dtype=torch.float32, device=q_noise.device)
+    lse_ptr = None if lse is None else lse.data_ptr()
+    kc = _bf16(k_cond, "k_cond") if C > 0 else None
+    vc = _bf16(v_cond, "v_cond") if C > 0 else None
+    _check(lib().lcv_bsa_forward_cached(_bf16(q_noise, "q_noise"), _bf16(k_noise, "k_noise"),
+                                        _bf16(v_noise, "v_noise"), kc, vc, B, Hh, layout.handle, C, flags,
+                                        ctypes.byref(g.c()) if g is not None else None, _bf16(out, "out"),
+                                        lse_ptr, _stream_ptr(stream)))
+    return out, lse

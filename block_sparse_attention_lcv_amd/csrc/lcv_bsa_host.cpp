@@ -1,0 +1,346 @@
+// Host side of liblcv_bsa: argument validation, layout handles and kernel launches.
+// Every check runs before anything is launched; see include/lcv_bsa.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "lcv_internal.h"
+
+struct lcv_bsa_layout {
+  lcv_bsa_layout_info info;
+  lcv::LayoutDev dev;
+  int device;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lcv_status fail(lcv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+lcv_status ok() {
+  g_last_error.clear();
+  return LCV_OK;
+}
+
+lcv_status hip_fail(hipError_t e, const char* what) {
+  return fail(LCV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+lcv_status check_params(const lcv_bsa_layout_params* p) {
+  if (p == nullptr) return fail(LCV_ERR_NULL, "params is NULL");
+  if (p->block != LCV_BLOCK) return fail(LCV_ERR_INVALID_ARG, "block must be %d (got %d)", LCV_BLOCK, p->block);
+  if (p->n_tokens < 1) return fail(LCV_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", p->n_tokens);
+  if (p->local_blocks < 0) return fail(LCV_ERR_INVALID_ARG, "local_blocks must be >= 0 (got %d)", p->local_blocks);
+  if (p->global_stride < 0) return fail(LCV_ERR_INVALID_ARG, "global_stride must be >= 0 (got %d)", p->global_stride);
+  if (p->cond_len < 0 || p->cond_len > p->n_tokens)
+    return fail(LCV_ERR_INVALID_ARG, "cond_len must be in [0, n_tokens] (got %d, n_tokens %d)", p->cond_len, p->n_tokens);
+  const int64_t n = ((int64_t)p->n_tokens + LCV_BLOCK - 1) / LCV_BLOCK;
+  if (n >= (int64_t(1) << 23))
+    return fail(LCV_ERR_UNSUPPORTED, "more than 2^23 blocks (%lld) are not supported", (long long)n);
+  return LCV_OK;
+}
+
+lcv::LayoutRule make_rule(const lcv_bsa_layout_params* p) {
+  lcv::LayoutRule L;
+  L.N = p->n_tokens;
+  L.n = (p->n_tokens + LCV_BLOCK - 1) / LCV_BLOCK;
+  L.C = p->cond_len;
+  // a window wider than the sequence is the whole sequence
+  L.w = p->local_blocks < L.n ? p->local_blocks : L.n;
+  L.s = p->global_stride;
+  L.jc = (p->cond_len + LCV_BLOCK - 1) / LCV_BLOCK;
+  return L;
+}
+
+// Closed-form sizes of the layout (host only).
+lcv_status compute_info(const lcv_bsa_layout_params* p, lcv_bsa_layout_info* info) {
+  const lcv::LayoutRule L = make_rule(p);
+  int64_t nnz = 0, pairs = 0;
+  int32_t max_len = 0;
+  const int32_t last_size = L.N - 64 * (L.n - 1);
+  const int32_t fc = L.C / 64;                       // blocks [0, fc) are all condition keys
+  const int32_t partial = (fc < L.n) ? (L.C - 64 * fc) : 0;  // condition keys of block fc
+  for (int32_t i = 0; i < L.n; ++i) {
+    const lcv::RowShape rs = lcv::row_shape(L, i);
+    nnz += rs.len;
+    if (rs.len > max_len) max_len = rs.len;
+    const int32_t size_i = (i == L.n - 1) ? last_size : 64;
+    int32_t cond_rows = L.C - 64 * i;
+    cond_rows = cond_rows < 0 ? 0 : (cond_rows > size_i ? size_i : cond_rows);
+    const int32_t noise_rows = size_i - cond_rows;
+    // keys of the row: 64 per block, the last block may be short
+    int64_t keys = 64 * (int64_t)rs.len;
+    if (lcv::row_has(L, rs, L.n - 1)) keys -= 64 - last_size;
+    // condition keys of the row
+    int64_t ckeys = 64 * (int64_t)lcv::row_count_below(L, rs, fc);
+    if (partial > 0 && lcv::row_has(L, rs, fc)) ckeys += partial;
+    pairs += (int64_t)noise_rows * keys + (int64_t)cond_rows * ckeys;
+  }
+  if (nnz >= (int64_t(1) << 31))
+    return fail(LCV_ERR_UNSUPPORTED, "layout has %lld entries; at most 2^31-1 are supported", (long long)nnz);
+  info->n_tokens = p->n_tokens;
+  info->n_blocks = L.n;
+  info->local_blocks = p->local_blocks;
+  info->global_stride = p->global_stride;
+  info->cond_len = p->cond_len;
+  info->max_row_len = max_len;
+  info->nnz = nnz;
+  info->attended_pairs = pairs;
+  return LCV_OK;
+}
+
+lcv_status check_grid(const lcv_rope3d_grid* grid) {
+  if (grid == nullptr) return fail(LCV_ERR_NULL, "grid is NULL");
+  if (grid->T < 1 || grid->H < 1 || grid->W < 1)
+    return fail(LCV_ERR_INVALID_ARG, "grid dimensions must be >= 1 (got %d x %d x %d)", grid->T, grid->H, grid->W);
+  if (!(grid->theta > 0.f) || !std::isfinite(grid->theta))
+    return fail(LCV_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if ((int64_t)grid->T * grid->H * grid->W >= (int64_t(1) << 31))
+    return fail(LCV_ERR_UNSUPPORTED, "grid has more than 2^31-1 tokens");
+  return LCV_OK;
+}
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_cond;
+  const void* v_cond;
+  void* out;
+  float* lse;
+  bool cached;
+};
+
+lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
+                          int32_t cond_len, uint32_t flags, const lcv_rope3d_grid* grid, hipStream_t stream) {
+  if (layout == nullptr) return fail(LCV_ERR_NULL, "layout is NULL");
+  if (batch < 1 || heads < 1) return fail(LCV_ERR_INVALID_ARG, "batch and heads must be >= 1 (got %d, %d)", batch, heads);
+  const lcv_bsa_layout_info& info = layout->info;
+  if (cond_len != info.cond_len)
+    return fail(LCV_ERR_LAYOUT_MISMATCH, "cond_len %d differs from the layout's %d", cond_len, info.cond_len);
+  if (flags & ~(LCV_ROPE_Q | LCV_ROPE_K)) return fail(LCV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const int32_t N = info.n_tokens, C = info.cond_len;
+  const bool has_noise = N > C;
+  if (a.cached) {
+    if (has_noise && (a.q == nullptr || a.k == nullptr || a.v == nullptr || a.out == nullptr))
+      return fail(LCV_ERR_NULL, "q_noise, k_noise, v_noise and out_noise are required when cond_len < n_tokens");
+    if (C > 0 && (a.k_cond == nullptr || a.v_cond == nullptr))
+      return fail(LCV_ERR_NULL, "k_cond and v_cond are required when cond_len > 0");
+  } else if (a.q == nullptr || a.k == nullptr || a.v == nullptr || a.out == nullptr) {
+    return fail(LCV_ERR_NULL, "q, k, v and out are required");
+  }
+  const void* ptrs16[] = {a.q, a.k, a.v, a.k_cond, a.v_cond, a.out};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (a.lse != nullptr && !aligned(a.lse, 4)) return fail(LCV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  int32_t rope_entries = 0;
+  if (flags) {
+    lcv_status st = check_grid(grid);
+    if (st != LCV_OK) return st;
+    if ((int64_t)grid->T * grid->H * grid->W != N)
+      return fail(LCV_ERR_SHAPE, "grid %d x %d x %d has %lld tokens, layout has %d", grid->T, grid->H, grid->W,
+                  (long long)grid->T * grid->H * grid->W, N);
+    const int64_t entries = 8 * (int64_t)grid->T + 12 * (int64_t)grid->H + 12 * (int64_t)grid->W;
+    if (entries > lcv::kMaxRopeEntries)
+      return fail(LCV_ERR_UNSUPPORTED, "fused RoPE supports 8T+12H+12W <= %d (got %lld); rotate with lcv_rope3d_apply",
+                  lcv::kMaxRopeEntries, (long long)entries);
+    rope_entries = (int32_t)entries;
+  }
+  const int64_t bh = (int64_t)batch * heads;
+  const int32_t n = info.n_blocks;
+  const int32_t q_row0 = a.cached ? C : 0;
+  if (q_row0 >= N) return ok();   // cached call with no noise tokens
+  const int32_t st_first = (q_row0 / 64) / lcv::kWaves;
+  const int32_t n_st = layout->dev.n_st;
+  const int64_t n_items = bh * (n_st - st_first);
+  if (n_items >= (int64_t(1) << 31) - 8)
+    return fail(LCV_ERR_UNSUPPORTED, "batch*heads*workgroups = %lld is too large", (long long)n_items);
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != layout->device)
+    return fail(LCV_ERR_INVALID_ARG, "layout was built on device %d, current device is %d", layout->device, dev);
+
+  lcv::FwdParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.k_cond = static_cast<const uint16_t*>(a.k_cond);
+  p.v_cond = static_cast<const uint16_t*>(a.v_cond);
+  p.out = static_cast<uint16_t*>(a.out);
+  p.lse = a.lse;
+  p.row_ptr = layout->dev.row_ptr;
+  p.st_cnt = layout->dev.st_cnt;
+  p.st_ent = layout->dev.st_ent;
+  p.N = N;
+  p.C = C;
+  p.n_blocks = n;
+  p.q_row0 = q_row0;
+  p.q_rows = N - q_row0;
+  p.kv_split = a.cached ? C : 0;
+  p.st_first = st_first;
+  p.n_st_active = n_st - st_first;
+  p.n_items = (int32_t)n_items;
+  p.flags = flags;
+  if (flags) {
+    p.T = grid->T;
+    p.H = grid->H;
+    p.W = grid->W;
+    p.div_hw = lcv::make_fastdiv((uint32_t)grid->H * (uint32_t)grid->W);
+    p.div_w = lcv::make_fastdiv((uint32_t)grid->W);
+    p.log2_theta = std::log2(grid->theta);
+    p.rope_entries = rope_entries;
+  }
+  e = lcv::launch_bsa_fwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_fwd launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lcv_abi_version(void) { return LCV_BSA_ABI_VERSION; }
+
+const char* lcv_last_error(void) { return g_last_error.c_str(); }
+
+lcv_status lcv_bsa_layout_query(const lcv_bsa_layout_params* params, lcv_bsa_layout_info* info) {
+  lcv_status st = check_params(params);
+  if (st != LCV_OK) return st;
+  if (info == nullptr) return fail(LCV_ERR_NULL, "info is NULL");
+  st = compute_info(params, info);
+  if (st != LCV_OK) return st;
+  return ok();
+}
+
+lcv_status lcv_bsa_build_layout(const lcv_bsa_layout_params* params, hipStream_t stream, lcv_bsa_layout** out) {
+  if (out == nullptr) return fail(LCV_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  lcv_status st = check_params(params);
+  if (st != LCV_OK) return st;
+  lcv_bsa_layout_info info;
+  st = compute_info(params, &info);
+  if (st != LCV_OK) return st;
+
+  lcv_bsa_layout* h = new (std::nothrow) lcv_bsa_layout;
+  if (h == nullptr) return fail(LCV_ERR_OOM, "host allocation failed");
+  std::memset(h, 0, sizeof *h);
+  h->info = info;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  const int32_t n = info.n_blocks;
+  h->dev.n_st = (n + lcv::kWaves - 1) / lcv::kWaves;
+  const size_t nnz_alloc = info.nnz > 0 ? (size_t)info.nnz : 1;
+  struct {
+    int32_t** p;
+    size_t count;
+  } bufs[] = {{&h->dev.row_ptr, (size_t)n + 1}, {&h->dev.col_idx, nnz_alloc},
+              {&h->dev.st_cnt, (size_t)h->dev.n_st}, {&h->dev.st_ent, nnz_alloc}};
+  for (auto& b : bufs) {
+    e = hipMalloc(reinterpret_cast<void**>(b.p), b.count * sizeof(int32_t));
+    if (e != hipSuccess) {
+      lcv_bsa_layout_destroy(h);
+      return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "hipMalloc of the layout: %s",
+                  hipGetErrorString(e));
+    }
+  }
+  const lcv::LayoutRule L = make_rule(params);
+  e = lcv::launch_layout_build(L, h->dev, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  int32_t gpu_nnz = -1;
+  if (e == hipSuccess) e = hipMemcpy(&gpu_nnz, h->dev.row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) {
+    lcv_bsa_layout_destroy(h);
+    return hip_fail(e, "layout build");
+  }
+  if (gpu_nnz != info.nnz) {
+    lcv_bsa_layout_destroy(h);
+    return fail(LCV_ERR_HIP, "layout build produced %d entries, expected %lld", gpu_nnz, (long long)info.nnz);
+  }
+  *out = h;
+  return ok();
+}
+
+lcv_status lcv_bsa_layout_get_info(const lcv_bsa_layout* layout, lcv_bsa_layout_info* info) {
+  if (layout == nullptr || info == nullptr) return fail(LCV_ERR_NULL, "layout and info are required");
+  *info = layout->info;
+  return ok();
+}
+
+lcv_status lcv_bsa_layout_copy_csr(const lcv_bsa_layout* layout, int32_t* row_ptr, int32_t* col_idx,
+                                   hipStream_t stream) {
+  if (layout == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return fail(LCV_ERR_NULL, "layout, row_ptr and col_idx are required");
+  if (!aligned(row_ptr, 4) || !aligned(col_idx, 4)) return fail(LCV_ERR_INVALID_ARG, "int32 buffers must be 4-byte aligned");
+  hipError_t e = hipMemcpyAsync(row_ptr, layout->dev.row_ptr, ((size_t)layout->info.n_blocks + 1) * sizeof(int32_t),
+                                hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && layout->info.nnz > 0)
+    e = hipMemcpyAsync(col_idx, layout->dev.col_idx, (size_t)layout->info.nnz * sizeof(int32_t),
+                       hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy csr");
+  return ok();
+}
+
+void lcv_bsa_layout_destroy(lcv_bsa_layout* layout) {
+  if (layout == nullptr) return;
+  (void)hipFree(layout->dev.row_ptr);
+  (void)hipFree(layout->dev.col_idx);
+  (void)hipFree(layout->dev.st_cnt);
+  (void)hipFree(layout->dev.st_ent);
+  delete layout;
+}
+
+lcv_status lcv_rope3d_apply(const void* x, void* y, int64_t n_outer, int32_t n_tokens, int32_t token_offset,
+                            const lcv_rope3d_grid* grid, hipStream_t stream) {
+  if (x == nullptr || y == nullptr) return fail(LCV_ERR_NULL, "x and y are required");
+  if (n_outer < 0 || n_tokens < 0 || token_offset < 0)
+    return fail(LCV_ERR_INVALID_ARG, "n_outer, n_tokens and token_offset must be >= 0");
+  lcv_status st = check_grid(grid);
+  if (st != LCV_OK) return st;
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(LCV_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  const int64_t total = (int64_t)grid->T * grid->H * grid->W;
+  if ((int64_t)token_offset + n_tokens > total)
+    return fail(LCV_ERR_SHAPE, "tokens [%d, %lld) exceed the grid's %lld tokens", token_offset,
+                (long long)token_offset + n_tokens, (long long)total);
+  if (n_outer > (int64_t)65535 * 8) return fail(LCV_ERR_UNSUPPORTED, "n_outer above 524280 is not supported");
+  const hipError_t e = lcv::launch_rope3d(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), n_outer, n_tokens,
+                                          token_offset, grid->H, grid->W, std::log2(grid->theta), stream);
+  if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+  return ok();
+}
+
+lcv_status lcv_bsa_forward(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
+                           const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
+                           const lcv_rope3d_grid* grid, void* out, float* lse, hipStream_t stream) {
+  FwdArgs a{q, k, v, nullptr, nullptr, out, lse, false};
+  return forward_common(a, batch, heads, layout, cond_len, flags, grid, stream);
+}
+
+lcv_status lcv_bsa_forward_cached(const void* q_noise, const void* k_noise, const void* v_noise, const void* k_cond,
+                                  const void* v_cond, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
+                                  int32_t cond_len, uint32_t flags, const lcv_rope3d_grid* grid, void* out_noise,
+                                  float* lse_noise, hipStream_t stream) {
+  FwdArgs a{q_noise, k_noise, v_noise, k_cond, v_cond, out_noise, lse_noise, true};
+  return forward_common(a, batch, heads, layout, cond_len, flags, grid, stream);
+}
+
+}  // extern "C"

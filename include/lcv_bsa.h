@@ -1,0 +1,178 @@
+/*
+ * lcv_bsa.h -- C ABI of the LongCat-Video block-sparse 3D self-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the self-attention of the LongCat-Video diffusion transformer over
+ * patchified video latent tokens:
+ *   - tokens are the latent grid (T, H, W) flattened row-major in (t, y, x); condition
+ *     frames come first along time (myzaker article on LongCat-Video, section on the
+ *     technical principles: noise-free condition frames and noisy frames concatenated on
+ *     the time axis; the number of condition frames selects text-, image- or
+ *     video-conditioned generation);
+ *   - attention runs over blocks of 64 consecutive tokens; query block i attends key
+ *     block j iff |i - j| <= local_blocks or j % global_stride == 0 (longcat-video-rs page,
+ *     section 02 benchmark table "block=64, local=2, stride=4" and section 03
+ *     "Block-Sparse & Multi-Audio"; zhichai.net post, section "Block Sparse Attention":
+ *     dense inside a block pair, sparse between blocks);
+ *   - condition tokens (the first cond_len tokens) attend only to condition tokens, so
+ *     their keys and values can be cached and reused across calls (myzaker article,
+ *     technical principles: block attention with a KV cache);
+ *   - queries and keys carry a partitioned 3D rotary embedding: channels [0,16) turn with
+ *     t, [16,40) with y, [40,64) with x, adjacent channel pairs as complex numbers, pair p
+ *     of a section of width d at angle pos * theta^(-2p/d) (longcat-video-rs page, section
+ *     03 "Partitioned 3D-RoPE (16T+24H+24W)").
+ *
+ * Numerics: bf16 inputs, RoPE in fp32 rounded to bf16 before the matrix cores, scores
+ * and softmax in fp32 with fp32 accumulation, probabilities rounded to bf16 for the
+ * P*V product, bf16 output, fp32 natural-log LSE of the scores scaled by 1/sqrt(64).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are caller-owned device memory, contiguous, row-major, with the shapes
+ *     stated below; bf16 tensors are passed as void* and must be 16-byte aligned, fp32
+ *     tensors 4-byte aligned.  The library never frees them and no forward or RoPE call
+ *     allocates memory.
+ *   - Calls are asynchronous on the given stream (0 = the null stream) and never
+ *     synchronise, except lcv_bsa_build_layout (see there).  Results are bitwise
+ *     deterministic for identical inputs on the same GPU.
+ *   - Every argument is validated on the host before anything is launched: on error the
+ *     status says why, nothing is launched and lcv_last_error() holds a message.  HIP
+ *     failures are reported as LCV_ERR_HIP.
+ *   - A layout is immutable after it is built and may be shared by concurrent calls on
+ *     any streams and threads.
+ */
+#ifndef LCV_BSA_H
+#define LCV_BSA_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCV_BSA_ABI_VERSION 1
+#define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
+#define LCV_BLOCK 64      /* tokens per attention block */
+
+typedef enum lcv_status {
+  LCV_OK = 0,
+  LCV_ERR_NULL = 1,            /* a required pointer is NULL */
+  LCV_ERR_INVALID_ARG = 2,     /* a value is out of range or a pointer is misaligned */
+  LCV_ERR_SHAPE = 3,           /* sizes disagree (e.g. N != T*H*W) */
+  LCV_ERR_LAYOUT_MISMATCH = 5, /* cond_len differs from the one the layout was built for */
+  LCV_ERR_UNSUPPORTED = 6,     /* valid but beyond what this build supports (sizes) */
+  LCV_ERR_OOM = 7,             /* device allocation failed (layout build only) */
+  LCV_ERR_HIP = 8              /* a HIP runtime call failed */
+} lcv_status;
+
+/* flags of the forward calls: apply the 3D-RoPE to Q and/or K while loading them.
+ * Without a flag the corresponding input is taken as already rotated. */
+#define LCV_ROPE_Q 1u
+#define LCV_ROPE_K 2u
+
+/* Block layout parameters.  n_tokens = N >= 1; block must be 64; local_blocks = w >= 0
+ * (window radius in blocks); global_stride = s >= 0 (0 disables global blocks, 1 makes
+ * every key block global); cond_len = C in [0, N] (condition tokens [0, C)). */
+typedef struct lcv_bsa_layout_params {
+  int32_t n_tokens;
+  int32_t block;
+  int32_t local_blocks;
+  int32_t global_stride;
+  int32_t cond_len;
+} lcv_bsa_layout_params;
+
+/* Latent grid of the 3D-RoPE: tokens are (t, y, x) row-major with t < T, y < H, x < W;
+ * theta is the rotary base (1e4 for LongCat-Video). */
+typedef struct lcv_rope3d_grid {
+  int32_t T;
+  int32_t H;
+  int32_t W;
+  float theta;
+} lcv_rope3d_grid;
+
+typedef struct lcv_bsa_layout_info {
+  int32_t n_tokens;
+  int32_t n_blocks;        /* ceil(N / 64) */
+  int32_t local_blocks;
+  int32_t global_stride;
+  int32_t cond_len;
+  int32_t max_row_len;     /* longest CSR row */
+  int64_t nnz;             /* CSR entries: block pairs holding >= 1 attended token pair */
+  int64_t attended_pairs;  /* (q, k) token pairs attended, per (batch, head) */
+} lcv_bsa_layout_info;
+
+typedef struct lcv_bsa_layout lcv_bsa_layout; /* opaque */
+
+/* Sizes of the layout that lcv_bsa_build_layout would build, computed on the host in
+ * closed form without touching the GPU.  Errors: NULL, INVALID_ARG, UNSUPPORTED
+ * (nnz >= 2^31). */
+lcv_status lcv_bsa_layout_query(const lcv_bsa_layout_params* params, lcv_bsa_layout_info* info);
+
+/* Build the block layout on the GPU: the CSR (row_ptr[n+1], ascending col_idx[nnz], int32)
+ * of key blocks per query block -- block pairs of the rule above that hold at least one
+ * token pair allowed by the condition rule -- plus the internal schedule the forward
+ * kernels walk.  Allocates device memory owned by the returned handle and waits for the
+ * stream before returning (built once per shape, reused across steps, layers, heads and
+ * batch items).  Errors: NULL, INVALID_ARG, UNSUPPORTED, OOM, HIP; *out is NULL on error. */
+lcv_status lcv_bsa_build_layout(const lcv_bsa_layout_params* params, hipStream_t stream,
+                                lcv_bsa_layout** out);
+
+/* Sizes of a built layout.  Errors: NULL. */
+lcv_status lcv_bsa_layout_get_info(const lcv_bsa_layout* layout, lcv_bsa_layout_info* info);
+
+/* Copy the CSR into caller-owned device buffers row_ptr[n_blocks+1] and col_idx[nnz]
+ * (int32), asynchronously on stream.  Errors: NULL, INVALID_ARG (misaligned), HIP. */
+lcv_status lcv_bsa_layout_copy_csr(const lcv_bsa_layout* layout, int32_t* row_ptr, int32_t* col_idx,
+                                   hipStream_t stream);
+
+/* Release a layout (NULL is a no-op).  The caller must ensure no queued call still uses it. */
+void lcv_bsa_layout_destroy(lcv_bsa_layout* layout);
+
+/* Apply the partitioned 3D-RoPE to x[n_outer, n_tokens, 64] (bf16) and write y (bf16, may be
+ * equal to x for in-place use; must not otherwise overlap x).  Row r of each of the n_outer
+ * slices (batch * heads) is token token_offset + r of the grid, so noise tokens of a cached
+ * call pass token_offset = cond_len.  Math in fp32, result rounded to nearest even bf16.
+ * Errors: NULL, INVALID_ARG (n_outer < 0, n_tokens < 0, token_offset < 0, theta <= 0,
+ * misalignment), SHAPE (token_offset + n_tokens > T*H*W), HIP. */
+lcv_status lcv_rope3d_apply(const void* x, void* y, int64_t n_outer, int32_t n_tokens,
+                            int32_t token_offset, const lcv_rope3d_grid* grid, hipStream_t stream);
+
+/* Block-sparse attention over all N tokens.
+ *   q, k, v : bf16 [batch, heads, N, 64], N = layout n_tokens
+ *   out     : bf16 [batch, heads, N, 64]
+ *   lse     : fp32 [batch, heads, N] natural-log LSE of the scaled scores, or NULL
+ *   cond_len: must equal the layout's (LCV_ERR_LAYOUT_MISMATCH otherwise)
+ *   flags   : LCV_ROPE_Q | LCV_ROPE_K subset; grid is required (N == T*H*W) iff a flag is set
+ * A query row with no attended key (impossible with the layouts above) gets out = 0 and
+ * lse = -inf.  Errors: NULL, INVALID_ARG, SHAPE, LAYOUT_MISMATCH, UNSUPPORTED, HIP. */
+lcv_status lcv_bsa_forward(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
+                           const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
+                           const lcv_rope3d_grid* grid, void* out, float* lse, hipStream_t stream);
+
+/* Block-sparse attention of the noise tokens [C, N) only, with the condition keys and
+ * values taken from a cache (C = cond_len, N = layout n_tokens):
+ *   q_noise, k_noise, v_noise : bf16 [batch, heads, N-C, 64] (token C+r at row r)
+ *   k_cond, v_cond            : bf16 [batch, heads, C, 64], the condition K/V exactly as a
+ *                               full call received them (raw K if LCV_ROPE_K is set,
+ *                               pre-rotated K otherwise); may be NULL when C == 0
+ *   out_noise                 : bf16 [batch, heads, N-C, 64]; lse_noise fp32 [batch, heads, N-C] or NULL
+ * Results equal rows [C, N) of lcv_bsa_forward on the concatenated sequence, bitwise.
+ * C == N is a valid no-op.  Errors as lcv_bsa_forward. */
+lcv_status lcv_bsa_forward_cached(const void* q_noise, const void* k_noise, const void* v_noise,
+                                  const void* k_cond, const void* v_cond, int32_t batch, int32_t heads,
+                                  const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
+                                  const lcv_rope3d_grid* grid, void* out_noise, float* lse_noise,
+                                  hipStream_t stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* lcv_last_error(void);
+
+/* LCV_BSA_ABI_VERSION of the loaded library. */
+int32_t lcv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCV_BSA_H */

@@ -1,0 +1,118 @@
+"""C-ABI library on the CPU: it loads, exports every declared symbol, its host-side
+layout arithmetic matches the oracle, and argument errors are reported before anything
+touches the GPU (no compute calls here)."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_lcv_amd as bsa
+import oracle
+from lcv_inputs import WORKLOADS
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "lcv_bsa.h"
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = bsa.lib()
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert sorted(bsa.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version():
+    assert bsa.lib().lcv_abi_version() == 1
+
+
+QUERY_CASES = [
+    (512, 0, 2, 4), (37440, 0, 2, 4), (37440, 1560, 2, 4), (86400, 0, 2, 4), (62400, 24960, 2, 4),
+    (62400, 24960, 64, 3), (62400, 24960, 2, 16), (630, 210, 2, 4), (630, 630, 1, 3), (1, 0, 2, 4),
+    (63, 5, 0, 0), (65, 64, 0, 1), (1000, 999, 3, 5), (4097, 100, 7, 0), (5000, 64 * 13, 100, 2),
+    (300, 63, 0, 3), (300, 127, 1, 2),
+]
+
+
+@pytest.mark.parametrize("n,c,w,s", QUERY_CASES)
+def test_layout_query_matches_oracle(n, c, w, s):
+    info = bsa.layout_query(n, w, s, c)
+    row_ptr, col_idx = oracle.csr(n, c, w, s)
+    lens = np.diff(row_ptr)
+    assert info["n_blocks"] == oracle.n_blocks_of(n)
+    assert info["nnz"] == col_idx.size
+    assert info["max_row_len"] == int(lens.max())
+    assert info["attended_pairs"] == oracle.attended_pairs(n, c, w, s)
+
+
+def test_workload_flop_counts():
+    """Effective FLOPs (4 * 64 * attended pairs * heads) of the five workloads."""
+    expected = {"tiny": 8.808e7, "t2v480": 2.959e12, "i2v480": 2.844e12, "t2v720": 1.548e13, "vc480": 6.194e12}
+    for name, w in WORKLOADS.items():
+        info = bsa.layout_query(w.n_tokens, w.local_blocks, w.global_stride, w.cond_len)
+        flops = 4 * 64 * info["attended_pairs"] * w.heads * w.batch
+        assert abs(flops / expected[name] - 1) < 1e-3, (name, flops)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_layout_param_errors():
+    L = bsa.lib()
+    info = bsa.LayoutInfo()
+    bad = [
+        (bsa.LayoutParams(0, 64, 2, 4, 0), 2),        # no tokens
+        (bsa.LayoutParams(128, 32, 2, 4, 0), 2),      # block must be 64
+        (bsa.LayoutParams(128, 64, -1, 4, 0), 2),     # negative window
+        (bsa.LayoutParams(128, 64, 2, -4, 0), 2),     # negative stride
+        (bsa.LayoutParams(128, 64, 2, 4, 129), 2),    # cond_len > N
+        (bsa.LayoutParams(128, 64, 2, 4, -1), 2),
+        (bsa.LayoutParams(2**30, 64, 2, 1, 0), 6),    # too many blocks
+    ]
+    for params, code in bad:
+        assert L.lcv_bsa_layout_query(ctypes.byref(params), ctypes.byref(info)) == code
+        assert L.lcv_last_error()
+    # the build entry point rejects the same parameters before touching the GPU
+    handle = ctypes.c_void_p(1234)
+    assert L.lcv_bsa_build_layout(ctypes.byref(bad[0][0]), None, ctypes.byref(handle)) == 2
+    assert handle.value is None
+    assert L.lcv_bsa_build_layout(None, None, ctypes.byref(handle)) == 1
+    assert L.lcv_bsa_layout_query(None, ctypes.byref(info)) == 1
+    assert L.lcv_bsa_layout_query(ctypes.byref(bsa.LayoutParams(128, 64, 2, 4, 0)), None) == 1
+    assert L.lcv_bsa_build_layout(ctypes.byref(bsa.LayoutParams(128, 64, 2, 4, 0)), None, None) == 1
+
+
+def test_forward_requires_layout():
+    L = bsa.lib()
+    g = bsa.Rope3dGrid(1, 1, 64, 1e4)
+    p = ctypes.c_void_p(4096)
+    assert L.lcv_bsa_forward(p, p, p, 1, 1, None, 0, 3, ctypes.byref(g), p, None, None) == 1
+    assert L.lcv_bsa_forward_cached(p, p, p, p, p, 1, 1, None, 0, 3, ctypes.byref(g), p, None, None) == 1
+    assert L.lcv_bsa_layout_get_info(None, None) == 1
+    assert L.lcv_bsa_layout_copy_csr(None, p, p, None) == 1
+    L.lcv_bsa_layout_destroy(None)   # no-op
+
+
+def test_rope_argument_errors():
+    L = bsa.lib()
+    g = bsa.Rope3dGrid(2, 4, 8, 1e4)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4098)
+    assert L.lcv_rope3d_apply(None, p, 1, 64, 0, ctypes.byref(g), None) == 1
+    assert L.lcv_rope3d_apply(p, p, 1, 64, 0, None, None) == 1
+    assert L.lcv_rope3d_apply(mis, p, 1, 64, 0, ctypes.byref(g), None) == 2
+    assert L.lcv_rope3d_apply(p, p, -1, 64, 0, ctypes.byref(g), None) == 2
+    assert L.lcv_rope3d_apply(p, p, 1, 64, 1, ctypes.byref(g), None) == 3       # 65 tokens > 64
+    bad_theta = bsa.Rope3dGrid(2, 4, 8, 0.0)
+    assert L.lcv_rope3d_apply(p, p, 1, 64, 0, ctypes.byref(bad_theta), None) == 2
+    bad_dims = bsa.Rope3dGrid(0, 4, 8, 1e4)
+    assert L.lcv_rope3d_apply(p, p, 1, 64, 0, ctypes.byref(bad_dims), None) == 2
