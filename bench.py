@@ -36,17 +36,80 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("bsa_fwd_kernel.hip", "lcv_internal.h", "rope_math.h")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the attention kernel's sources: a counter summary is valid only for the
+    kernel it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_lcv_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(path: str | None):
     """HBM bytes per launch of the attention kernel from a committed counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), if present."""
+    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration); None when absent or
+    taken on other kernel sources."""
     if not path or not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             data = json.load(f)
+        if data.get("kernel_source_sha256") != kernel_source_hash():
+            return None
         return float(data["bytes_per_launch"])
     except Exception:
         return None
+
+
+COPY_BYTES = 1 << 30
+
+
+def _pmc_rows(directory: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
+    return rows
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str) -> int:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by what the
+    same counters read for a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES)."""
+    result = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(directory, counter)
+        attn = [v for name, v, _ in rows if "bsa_fwd_kernel" in name]
+        # the calibration copies are the largest-grid copy dispatches
+        copy_rows = [(g, v) for name, v, g in rows if "copybuffer" in name.lower() or "copy_kernel" in name.lower()]
+        gmax = max((g for g, _ in copy_rows), default=0)
+        copies = [v for g, v in copy_rows if g == gmax]
+        if not attn or not copies:
+            print(f"no {counter} rows for the attention or copy kernel in {directory}", file=sys.stderr)
+            return 1
+        copy_kib = float(np.median(copies))
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        result[counter] = {"attn_kib_per_launch": float(np.median(attn)), "copy_kib": copy_kib,
+                           "scale_bytes_per_kib": scale * 1024.0, "launches": len(attn)}
+    fetch = result["FETCH_SIZE"]["attn_kib_per_launch"] * result["FETCH_SIZE"]["scale_bytes_per_kib"]
+    write = result["WRITE_SIZE"]["attn_kib_per_launch"] * result["WRITE_SIZE"]["scale_bytes_per_kib"]
+    result["bytes_per_launch"] = fetch + write
+    result["kernel_source_sha256"] = kernel_source_hash()
+    result["fetch_bytes"] = fetch
+    result["write_bytes"] = write
+    with open(out_path, "w") as f:
+        json.dump(result, f, indent=1)
+    print(json.dumps(result))
+    return 0
 
 
 def cpu_baseline(w, seconds: float = 12.0) -> dict:
@@ -89,11 +152,21 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t2v720", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-rope", action="store_true", help="inputs pre-rotated (no fused RoPE)")
+    ap.add_argument("--rope-mode", default="k-pass", choices=["k-pass", "fused", "none"],
+                    help="k-pass: K rotated by the standalone RoPE pass into a second buffer, Q rotated "
+                         "inside the attention kernel (both timed); fused: Q and K rotated inside the "
+                         "attention kernel; none: inputs taken as already rotated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --copy-calibration into "
+                         "HBM bytes per attention launch; writes --traffic-json and exits")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic, args.traffic_json)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -125,10 +198,20 @@ def main() -> int:
     del qb, kb, vb
     out = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device="cuda")
-    grid = None if args.no_rope else w.grid
+    k_rot = torch.empty_like(k) if args.rope_mode == "k-pass" else None
 
-    def step():
-        bsa.forward(q, k, v, layout, grid=grid, out=out, lse=lse)
+    # one step; ev_mid (if given) is recorded between the RoPE pass and the attention kernel
+    def step(ev_mid=None):
+        if args.rope_mode == "k-pass":
+            bsa.rope3d_apply(k, w.grid, out=k_rot)
+        if ev_mid is not None:
+            ev_mid.record(stream)
+        if args.rope_mode == "k-pass":
+            bsa.forward(q, k_rot, v, layout, grid=w.grid, rope_q=True, rope_k=False, out=out, lse=lse)
+        elif args.rope_mode == "fused":
+            bsa.forward(q, k, v, layout, grid=w.grid, out=out, lse=lse)
+        else:
+            bsa.forward(q, k, v, layout, grid=None, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -136,6 +219,7 @@ def main() -> int:
     log(f"[bench] warmup done ({args.warmup} steps)")
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
@@ -143,18 +227,20 @@ def main() -> int:
     t_all0.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
-        step()
+        step(mids[i])
         ends[i].record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
-    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    attn_ms = [m.elapsed_time(e) for m, e in zip(mids, ends)]
+    rope_ms = [s_.elapsed_time(m) for s_, m in zip(starts, mids)]
     ms_per_step = total_ms / args.steps
-    avg_launch_ms = float(np.mean(per_launch))
+    avg_launch_ms = float(np.mean(attn_ms))
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    log(f"[bench] {ms_per_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms "
-        f"(min {min(per_launch):.3f}, max {max(per_launch):.3f}), {value:.1f} TFLOP/s effective")
+    log(f"[bench] {ms_per_step:.3f} ms/step; attention kernel avg {avg_launch_ms:.3f} ms "
+        f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}); K RoPE pass avg {np.mean(rope_ms):.3f} ms; "
+        f"{value:.1f} TFLOP/s effective per step")
 
     result = {
         "metric": METRIC,
@@ -173,7 +259,10 @@ def main() -> int:
             "workload": f"{w.name}: {w.description}",
             "grid": list(w.grid), "tokens": w.n_tokens, "heads": w.heads, "head_dim": 64, "batch": w.batch,
             "cond_len": w.cond_len, "layout": f"block 64, local {w.local_blocks}, stride {w.global_stride}",
-            "rope": "none (pre-rotated)" if args.no_rope else "fused into Q/K loads",
+            "rope": {"k-pass": "Q rotated in the attention kernel's Q load, K by the standalone RoPE pass "
+                               "(both inside the timed step)",
+                     "fused": "Q and K rotated in the attention kernel's loads",
+                     "none": "none (inputs taken as rotated)"}[args.rope_mode],
             "nnz": info["nnz"], "attended_pairs_per_head": info["attended_pairs"],
             "effective_flops": flops,
         },
@@ -189,7 +278,17 @@ def main() -> int:
             "kernel": "bsa_fwd_kernel",
             "avg_launch_ms": round(avg_launch_ms, 4),
         },
+        "rope_pass_ms": round(float(np.mean(rope_ms)), 4) if args.rope_mode == "k-pass" else None,
     }
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {COPY_BYTES} bytes")
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

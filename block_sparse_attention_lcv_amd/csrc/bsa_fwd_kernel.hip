@@ -29,6 +29,8 @@
 //  * Workgroups are numbered so that each XCD (blockIdx % 8 on MI355X) receives a
 //    contiguous range of work items, i.e. whole heads: their shared global key blocks stay
 //    in that XCD's L2.
+#include <type_traits>
+
 #include "lcv_internal.h"
 #include "rope_math.h"
 
@@ -43,15 +45,17 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 64 * kWaves;
+#ifndef LCV_WAVES_PER_SIMD
+#define LCV_WAVES_PER_SIMD 2
+#endif
+constexpr int kWavesPerSimd = LCV_WAVES_PER_SIMD;  // occupancy the register budget is sized for
 constexpr int kTileBytes = 64 * 128;            // one 64 x 64 bf16 tile
 constexpr int kStageBytes = 2 * kTileBytes;     // K tile + V tile
 constexpr int kRopeTabOffset = 2 * kStageBytes; // two stages, then the cos/sin table
-constexpr int kChunksPerThread = 512 / kThreads; // 16-byte chunks of a tile per thread
 constexpr float kScoreToLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 constexpr float kRescaleLimit = 256.0f;                     // lazy-rescale threshold 2^8
 constexpr float kLn2 = 0.6931471805599453f;
 
-static_assert(512 % kThreads == 0, "tile chunks must split evenly over the workgroup");
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile; chunks are
 // XOR-swizzled by the row so that column reads of 8 consecutive rows hit distinct banks.
@@ -87,73 +91,121 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 raw, int c, const Coords& xyz,
   return raw;
 }
 
-__device__ __forceinline__ const uint16_t* key_row_ptr(const FwdParams& P, const uint16_t* cond, const uint16_t* noise,
-                                                       int bh, int key) {
-  if (key < P.kv_split) return cond + ((int64_t)bh * P.kv_split + key) * 64;
+// Staging of K/V block j into an LDS stage.  The 8 KB tile is moved as 8 wave-loads of
+// 1 KB (8 rows); wavefront w issues loads u = w*kLoadsPerWave + c.  In load u, lane l carries
+// row 8u + l/8 and lands at LDS byte 1024u + 16l, i.e. physical chunk l%8 of that row, which
+// holds logical chunk (l%8) ^ (row%8) under the XOR swizzle of tile_off.  Rows past the end
+// of the sequence read row N-1 (finite data; their scores are masked and their
+// probabilities are zero).
+constexpr int kLoadsPerWave = 8 / kWaves;
+static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <bool CACHED>
+__device__ __forceinline__ const uint16_t* kv_row(const FwdParams& P, const uint16_t* cond, const uint16_t* noise,
+                                                 int bh, int key) {
+  key = key < P.N ? key : P.N - 1;
+  if (CACHED && key < P.kv_split) return cond + ((int64_t)bh * P.kv_split + key) * 64;
   return noise + ((int64_t)bh * (P.N - P.kv_split) + (key - P.kv_split)) * 64;
 }
 
-__device__ __forceinline__ void load_kv(const FwdParams& P, int bh, int j, u32x4 (&kreg)[kChunksPerThread],
-                                        u32x4 (&vreg)[kChunksPerThread]) {
+// Issue the asynchronous global -> LDS copies of block j into stage `stage` (V always, K
+// too unless K is rotated on the way); K chunks to be rotated are loaded into kreg.
+template <bool ROPE_K, bool CACHED>
+__device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* stage, int bh, int j, int wave,
+                                            int lane, u32x4 (&kreg)[kLoadsPerWave]) {
+  const int gch = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) {
-    const int id = (int)threadIdx.x + c * kThreads;
-    const int row = id >> 3, ch = id & 7;
-    const int key = 64 * j + row;
-    if (key < P.N) {
-      kreg[c] = *reinterpret_cast<const u32x4*>(key_row_ptr(P, P.k_cond, P.k, bh, key) + 8 * ch);
-      vreg[c] = *reinterpret_cast<const u32x4*>(key_row_ptr(P, P.v_cond, P.v, bh, key) + 8 * ch);
-    } else {
-      kreg[c] = u32x4{0u, 0u, 0u, 0u};
-      vreg[c] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int c = 0; c < kLoadsPerWave; ++c) {
+    const int u = wave * kLoadsPerWave + c;
+    const int key = 64 * j + 8 * u + (lane >> 3);
+    const uint16_t* vsrc = kv_row<CACHED>(P, P.v_cond, P.v, bh, key) + 8 * gch;
+    __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(stage + kTileBytes + 1024 * u), 16, 0, 0);
+    const uint16_t* ksrc = kv_row<CACHED>(P, P.k_cond, P.k, bh, key) + 8 * gch;
+    if constexpr (ROPE_K)
+      kreg[c] = *reinterpret_cast<const u32x4*>(ksrc);
+    else
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(stage + 1024 * u), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_kv(const FwdParams& P, unsigned char* stage, int j, bool rope_k,
-                                         const float2* tab, u32x4 (&kreg)[kChunksPerThread],
-                                         const u32x4 (&vreg)[kChunksPerThread]) {
+// Rotate the K chunks loaded into kreg and write them to the stage (fused K RoPE only).
+__device__ __forceinline__ void stage_store_k(const FwdParams& P, unsigned char* stage, int j, int wave, int lane,
+                                              const float2* tab, const u32x4 (&kreg)[kLoadsPerWave]) {
+  const int gch = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) {
-    const int id = (int)threadIdx.x + c * kThreads;
-    const int row = id >> 3, ch = id & 7;
-    const int key = 64 * j + row;
+  for (int c = 0; c < kLoadsPerWave; ++c) {
+    const int u = wave * kLoadsPerWave + c;
+    const int key = 64 * j + 8 * u + (lane >> 3);
     u32x4 kv = kreg[c];
-    if (rope_k && key < P.N) kv = rope_chunk(kv, ch, token_coords((uint32_t)key, P), tab, P);
-    *reinterpret_cast<u32x4*>(stage + tile_off(row, ch)) = kv;
-    *reinterpret_cast<u32x4*>(stage + kTileBytes + tile_off(row, ch)) = vreg[c];
+    if (key < P.N) kv = rope_chunk(kv, gch, token_coords((uint32_t)key, P), tab, P);
+    *reinterpret_cast<u32x4*>(stage + 1024 * u + 16 * lane) = kv;
   }
 }
 
-// p = 2^(s * log2(e)/8 - mu) for the 32 scores of query tile qt held by this lane, packed to
-// bf16 as the B operand of the four 16-key P*V steps; returns the lane's sum of the
-// rounded probabilities.  (The bf16 pairs are built as bf16x2 values and fed to the dot2
-// intrinsic directly: taking them out of a u32 vector by bit_cast was mis-optimised by the
-// compiler into reusing one pair for several dot2 operands.)
-__device__ __forceinline__ float probs(const f32x16 (&s)[2][2], int qt, float mu, bf16x8 (&pb)[4]) {
+// p = 2^(s + shift) for the 16 scores of query tile qt held by this lane in one 32-key half
+// (the scores already include -m through the folded MFMA step), packed to bf16 as the B
+// operands of the two 16-key P*V steps; returns the lane's sum of the rounded
+// probabilities.  The bf16 pairs are built as bf16x2 values and fed to the dot2 intrinsic
+// directly: taking them out of a u32 vector by bit_cast was mis-optimised by the compiler
+// into reusing one pair for several dot2 operands.
+template <bool SHIFT>
+__device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb)[2]) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-  for (int js = 0; js < 4; ++js) {
-    const int kt = js >> 1, base = 8 * (js & 1);
+  for (int h = 0; h < 2; ++h) {
     bf16x2 w[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
-      const f32x2_t p = {__builtin_amdgcn_exp2f(fmaf(s[kt][qt][base + 2 * e2], kScoreToLog2, -mu)),
-                         __builtin_amdgcn_exp2f(fmaf(s[kt][qt][base + 2 * e2 + 1], kScoreToLog2, -mu))};
+      float x0 = s[8 * h + 2 * e2], x1 = s[8 * h + 2 * e2 + 1];
+      if (SHIFT) {
+        x0 += shift;
+        x1 += shift;
+      }
+      const f32x2_t p = {__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1)};
       w[e2] = __builtin_convertvector(p, bf16x2);
     }
     acc0 = __builtin_amdgcn_fdot2_f32_bf16(w[0], ones, acc0, false);
     acc1 = __builtin_amdgcn_fdot2_f32_bf16(w[1], ones, acc1, false);
     acc0 = __builtin_amdgcn_fdot2_f32_bf16(w[2], ones, acc0, false);
     acc1 = __builtin_amdgcn_fdot2_f32_bf16(w[3], ones, acc1, false);
-    pb[js] = __builtin_shufflevector(__builtin_shufflevector(w[0], w[1], 0, 1, 2, 3),
-                                     __builtin_shufflevector(w[2], w[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    pb[h] = __builtin_shufflevector(__builtin_shufflevector(w[0], w[1], 0, 1, 2, 3),
+                                    __builtin_shufflevector(w[2], w[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
   }
   return acc0 + acc1;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_kernel(const FwdParams P) {
+// B operand of the folded step: -m split into three bf16 parts (hi + mid + lo == -m to fp32
+// precision) in channels 0..2 of the lanes holding channel group 0.  Together with the A
+// operand of ones in the same channels, one extra MFMA step adds -m to every score.
+__device__ __forceinline__ bf16x8 fold_operand(float m, int g) {
+  const float nm = -m;
+  const __bf16 hi = (__bf16)nm;
+  const float r1 = nm - (float)hi;
+  const __bf16 mid = (__bf16)r1;
+  const __bf16 lo = (__bf16)(r1 - (float)mid);
+  const __bf16 z = (__bf16)0.0f;
+  const bf16x8 v = {hi, mid, lo, z, z, z, z, z};
+  const bf16x8 zero = {z, z, z, z, z, z, z, z};
+  return g == 0 ? v : zero;
+}
+
+// Q chunk (8 bf16 channels) -> bf16(value * log2(e)/8): the softmax scale and the change to
+// base 2 travel with Q into the matrix cores.
+__device__ __forceinline__ u32x4 scale_chunk(u32x4 raw) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = __uint_as_float(raw[e] << 16) * kScoreToLog2;
+    const float b = __uint_as_float(raw[e] & 0xffff0000u) * kScoreToLog2;
+    raw[e] = pack_bf16x2(a, b);
+  }
+  return raw;
+}
+
+template <bool ROPE_Q, bool ROPE_K, bool CACHED>
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const FwdParams P) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -167,12 +219,10 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_kernel(const FwdParams P)
   if (item >= P.n_items) return;
   const int bh = item / P.n_st_active;
   const int st = P.st_first + (item - bh * P.n_st_active);
-  const bool rope_q = (P.flags & LCV_ROPE_Q) != 0;
-  const bool rope_k = (P.flags & LCV_ROPE_K) != 0;
 
   // ---- cos/sin table of every (axis, position, pair) of the grid
   float2* tab = reinterpret_cast<float2*>(smem + kRopeTabOffset);
-  if (P.flags) {
+  if constexpr (ROPE_Q || ROPE_K) {
     for (int e = tid; e < P.rope_entries; e += kThreads) {
       int pos, p, width;
       if (e < 8 * P.T) {
@@ -186,11 +236,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_kernel(const FwdParams P)
       }
       tab[e] = rope_cos_sin(pos, p, width, P.log2_theta);
     }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // ---- this wavefront's query block, resident as MFMA B operands: qf[qt][ks] holds rows
-  // 32*qt + (lane & 31), channels 16*ks + 8*(lane >> 5) .. +7
+  // ---- this wavefront's query block as MFMA B operands: qf[qt][ks] holds rows
+  // 32*qt + (lane & 31), channels 16*ks + 8*(lane >> 5) .. +7, scaled by log2(e)/8
   const int qblk = st * kWaves + wave;
   const bool wave_on = (qblk < P.n_blocks) && (64 * qblk + 63 >= P.q_row0);
   bf16x8 qf[2][4];
@@ -202,23 +252,36 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_kernel(const FwdParams P)
     qok[qt] = wave_on && qtok[qt] >= P.q_row0 && qtok[qt] < P.N;
     const uint16_t* qrow = P.q + ((int64_t)bh * P.q_rows + (qtok[qt] - P.q_row0)) * 64;
     Coords xyz{0u, 0u, 0u};
-    if (rope_q && qok[qt]) xyz = token_coords((uint32_t)qtok[qt], P);
+    if (ROPE_Q && qok[qt]) xyz = token_coords((uint32_t)qtok[qt], P);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + g;
       u32x4 raw{0u, 0u, 0u, 0u};
       if (qok[qt]) {
         raw = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
-        if (rope_q) raw = rope_chunk(raw, c, xyz, tab, P);
+        if constexpr (ROPE_Q) raw = rope_chunk(raw, c, xyz, tab, P);
+        raw = scale_chunk(raw);
       }
       qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
-  // ---- walk the workgroup's key-block list
-  const int32_t* ents = P.st_ent + P.row_ptr[st * kWaves];
-  const int cnt = P.st_cnt[st];
+  // ---- per-lane LDS offsets (stage, 32-row and 16-row steps become immediates)
+  uint32_t ka_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
+  uint32_t vb_off[2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    const int krow0 = 4 * g + ((lane & 15) >> 2);
+    const int dcol = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    vb_off[dt] = tile_off(krow0, dcol >> 3) + (uint32_t)(lane & 1) * 8u;
+  }
 
+  const __bf16 one = (__bf16)1.0f, z = (__bf16)0.0f;
+  const bf16x8 ones_a = (g == 0) ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
+
+  // ---- state
   f32x16 o[2][2];   // O^T tiles [d tile][query tile]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -226,119 +289,193 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_kernel(const FwdParams P)
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[a][b][r] = 0.f;
-  float mref[2] = {-INFINITY, -INFINITY};
+  float mref[2] = {-INFINITY, -INFINITY};   // reference max of each row (log2 units), -inf = none yet
   float lsum[2] = {0.f, 0.f};
+  bf16x8 mneg[2] = {fold_operand(0.f, g), fold_operand(0.f, g)};
 
-  u32x4 kreg[kChunksPerThread], vreg[kChunksPerThread];
+  const int32_t* ents = P.st_ent + P.row_ptr[st * kWaves];
+  const int cnt = P.st_cnt[st];
+
+  u32x4 kreg[kLoadsPerWave];
   if (cnt > 0) {
     const int j0 = ents[0] >> 8;
-    load_kv(P, bh, j0, kreg, vreg);
-    store_kv(P, smem, j0, rope_k, tab, kreg, vreg);
+    stage_issue<ROPE_K, CACHED>(P, smem, bh, j0, wave, lane, kreg);
+    if constexpr (ROPE_K) stage_store_k(P, smem, j0, wave, lane, tab, kreg);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int e = 0; e < cnt; ++e) {
+  // S^T[key][query] - m = K Q'^T + (ones x -m) for the keys 32*kt .. 32*kt+31 of a stage
+  auto qk_half = [&](auto stage_tag, int kt, f32x16 (&s)[2]) {
+    constexpr uint32_t SB = decltype(stage_tag)::value * kStageBytes;
+    bf16x8 ka[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      ka[ks] = *reinterpret_cast<const bf16x8*>(smem + SB + ka_off[ks] + 4096u * kt);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, mneg[qt], acc, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qt][ks], acc, 0, 0, 0);
+      s[qt] = acc;
+    }
+  };
+
+  // token mask where the block pair crosses the end of the sequence or (full call) the
+  // condition boundary: keys >= N, and noise keys for condition queries
+  auto mask_half = [&](int key0, int kt, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = key < P.N && (qtok[qt] >= P.C || key < P.C);
+        if (!ok) s[qt][r] = -INFINITY;
+      }
+  };
+
+  // Online softmax of one half: p = 2^(s - m) with the row's reference m already folded into
+  // s.  The reference only moves when the row's probabilities in this half would exceed 2^8;
+  // the fast path is then one v_exp_f32, half a conversion and half a dot2 per score.
+  // Returns per query tile the change of the folded reference (0 when it did not move), which
+  // the caller applies to scores that were formed with the previous reference.
+  auto softmax_fast = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float (&psum)[2], bool (&trig)[2]) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      psum[qt] = probs<false>(s[qt], 0.f, pb[qt]);
+      const float row_sum = psum[qt] + partner(psum[qt]);
+      trig[qt] = (mref[qt] == -INFINITY) || !(row_sum <= kRescaleLimit);
+    }
+  };
+  auto softmax_slow = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float (&psum)[2], const bool (&trig)[2],
+                          float (&delta)[2]) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[qt][r]);
+      bm = fmaxf(bm, partner(bm));
+      const float m_fold = (mref[qt] == -INFINITY) ? 0.f : mref[qt];
+      const float m_new = trig[qt] ? fmaxf(mref[qt], bm + m_fold) : mref[qt];
+      const float alpha = (m_new == mref[qt]) ? 1.f : __builtin_amdgcn_exp2f(mref[qt] - m_new);
+      o[0][qt] *= alpha;
+      o[1][qt] *= alpha;
+      lsum[qt] *= alpha;
+      mref[qt] = m_new;
+      const float m_fold_new = (m_new == -INFINITY) ? 0.f : m_new;
+      delta[qt] = m_fold - m_fold_new;
+      psum[qt] = probs<true>(s[qt], delta[qt], pb[qt]);
+      mneg[qt] = fold_operand(m_fold_new, g);
+    }
+  };
+
+  // O^T[d][query] += V^T P^T over the two 16-key steps of half kt; V^T operands by
+  // transposing reads of the row-major V tile
+  auto pv_half = [&](auto stage_tag, int kt, const bf16x8 (&pb)[2][2]) {
+    constexpr uint32_t SB = decltype(stage_tag)::value * kStageBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t js_off = 2048u * (2 * kt + h);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(smem + SB + kTileBytes + vb_off[dt] + js_off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(smem + SB + kTileBytes + vb_off[dt] + js_off + 1024u));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qt][h], o[dt][qt], 0, 0, 0);
+      }
+    }
+  };
+
+  // One key block, its two halves software-pipelined: the second half's Q K^T is issued
+  // with the first half's softmax and the first half's P V with the second half's softmax,
+  // interleaved instruction by instruction, so one wavefront keeps the matrix cores and the
+  // vector ALU busy at the same time.  A rescale of the first half (rare) shifts the second
+  // half's scores by the change of the folded reference.
+  auto attend = [&](auto stage_tag, auto mask_tag, int j) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int key0 = 64 * j;
+    f32x16 s0[2], s1[2];
+    bf16x8 p0[2][2], p1[2][2];
+    float psum[2], delta[2];
+    bool trig[2];
+    qk_half(stage_tag, 0, s0);
+    if (MASK) mask_half(key0, 0, s0);
+    qk_half(stage_tag, 1, s1);
+    softmax_fast(s0, p0, psum, trig);
+    // 4 K reads, then 10 Q K^T MFMAs of the first half, then the second half's 10 MFMAs
+    // each followed by vector work of the first half's softmax
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+    if (__any(trig[0] || trig[1])) {
+      softmax_slow(s0, p0, psum, trig, delta);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s1[qt][r] += delta[qt];
+    }
+    lsum[0] += psum[0];
+    lsum[1] += psum[1];
+    pv_half(stage_tag, 0, p0);
+    if (MASK) mask_half(key0, 1, s1);
+    softmax_fast(s1, p1, psum, trig);
+    // 8 V^T reads, then the first half's 8 P V MFMAs each followed by vector work of the
+    // second half's softmax
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+    }
+    if (__any(trig[0] || trig[1])) softmax_slow(s1, p1, psum, trig, delta);
+    lsum[0] += psum[0];
+    lsum[1] += psum[1];
+    pv_half(stage_tag, 1, p1);
+  };
+
+  auto step = [&](auto stage_tag, int e) {
+    constexpr int STAGE = decltype(stage_tag)::value;
     const int ent = ents[e];
-    const int j = ent >> 8;
-    unsigned char* stage = smem + (e & 1) * kStageBytes;
+    const bool has_next = e + 1 < cnt;
     int jn = 0;
-    if (e + 1 < cnt) {
+    if (has_next) {
       jn = ents[e + 1] >> 8;
-      load_kv(P, bh, jn, kreg, vreg);
+      stage_issue<ROPE_K, CACHED>(P, smem + (1 - STAGE) * kStageBytes, bh, jn, wave, lane, kreg);
     }
-
     if (wave_on && ((ent >> wave) & 1)) {
-      // S^T[key][query] = K Q^T : s[kt][qt] covers keys 32*kt.., queries 32*qt..
-      f32x16 s[2][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 ka[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          ka[ks] = *reinterpret_cast<const bf16x8*>(stage + tile_off(32 * kt + l32, 2 * ks + g));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x16 acc;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qt][ks], acc, 0, 0, 0);
-          s[kt][qt] = acc;
-        }
-      }
-
-      // token mask where the block pair crosses the end of the sequence or the condition
-      // boundary: keys >= N, and noise keys for condition queries
-      const int key0 = 64 * j;
-      if (key0 + 63 >= P.N || (64 * qblk < P.C && key0 + 63 >= P.C)) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-              const bool ok = key < P.N && (qtok[qt] >= P.C || key < P.C);
-              if (!ok) s[kt][qt][r] = -INFINITY;
-            }
-      }
-
-      // online softmax (log2 domain, lazy rescaling)
-      bf16x8 pb[2][4];
-      float psum[2];
-      bool trig[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const bool uninit = mref[qt] == -INFINITY;
-        psum[qt] = probs(s, qt, uninit ? 0.f : mref[qt], pb[qt]);
-        const float row_sum = psum[qt] + partner(psum[qt]);
-        trig[qt] = uninit || !(row_sum <= kRescaleLimit);
-      }
-      if (__any(trig[0] || trig[1])) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          float bm = -INFINITY;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[kt][qt][r]);
-          bm = fmaxf(bm, partner(bm)) * kScoreToLog2;
-          const float m_new = trig[qt] ? fmaxf(mref[qt], bm) : mref[qt];
-          const float alpha = (m_new == mref[qt]) ? 1.f : __builtin_amdgcn_exp2f(mref[qt] - m_new);
-          o[0][qt] *= alpha;
-          o[1][qt] *= alpha;
-          lsum[qt] *= alpha;
-          mref[qt] = m_new;
-          psum[qt] = probs(s, qt, (m_new == -INFINITY) ? 0.f : m_new, pb[qt]);
-        }
-      }
-      lsum[0] += psum[0];
-      lsum[1] += psum[1];
-
-      // O^T[d][query] += V^T P^T : 16-key steps js, d tiles dt
-      const unsigned char* vt = stage + kTileBytes;
-#pragma unroll
-      for (int js = 0; js < 4; ++js) {
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int krow = 16 * js + 4 * g + ((lane & 15) >> 2);
-          const int dcol = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const uint32_t sub = (uint32_t)((dcol >> 2) & 1) * 8u;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vt + tile_off(krow, dcol >> 3) + sub));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vt + tile_off(krow + 8, dcol >> 3) + sub));
-          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qt][js], o[dt][qt], 0, 0, 0);
-        }
-      }
+      const int j = ent >> 8;
+      bool need_mask = 64 * j + 63 >= P.N;
+      if constexpr (!CACHED) need_mask = need_mask || (64 * qblk < P.C && 64 * j + 63 >= P.C);
+      if (need_mask)
+        attend(stage_tag, std::true_type{}, j);
+      else
+        attend(stage_tag, std::false_type{}, j);
     }
-
-    if (e + 1 < cnt) store_kv(P, smem + ((e + 1) & 1) * kStageBytes, jn, rope_k, tab, kreg, vreg);
+    if constexpr (ROPE_K) {
+      if (has_next) stage_store_k(P, smem + (1 - STAGE) * kStageBytes, jn, wave, lane, tab, kreg);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  int e = 0;
+  for (; e + 1 < cnt; e += 2) {
+    step(std::integral_constant<int, 0>{}, e);
+    step(std::integral_constant<int, 1>{}, e + 1);
   }
+  if (e < cnt) step(std::integral_constant<int, 0>{}, e);
 
   // ---- epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2
   if (wave_on) {
@@ -365,14 +502,30 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_kernel(const FwdParams P)
   }
 }
 
+template <bool ROPE_Q, bool ROPE_K, bool CACHED>
+hipError_t launch_variant(const FwdParams& p, unsigned groups, size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((bsa_fwd_kernel<ROPE_Q, ROPE_K, CACHED>), dim3(groups), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.n_items == 0) return hipSuccess;
   const unsigned groups = (unsigned)(((int64_t)p.n_items + 7) / 8 * 8);
-  const size_t lds = (size_t)kRopeTabOffset + (p.flags ? (size_t)p.rope_entries * sizeof(float2) : 0);
-  hipLaunchKernelGGL(bsa_fwd_kernel, dim3(groups), dim3(kThreads), lds, stream, p);
-  return hipGetLastError();
+  const bool rq = (p.flags & LCV_ROPE_Q) != 0, rk = (p.flags & LCV_ROPE_K) != 0, cached = p.kv_split > 0;
+  const size_t lds = (size_t)kRopeTabOffset + ((rq || rk) ? (size_t)p.rope_entries * sizeof(float2) : 0);
+  const int v = (rq ? 4 : 0) | (rk ? 2 : 0) | (cached ? 1 : 0);
+  switch (v) {
+    case 0: return launch_variant<false, false, false>(p, groups, lds, stream);
+    case 1: return launch_variant<false, false, true>(p, groups, lds, stream);
+    case 2: return launch_variant<false, true, false>(p, groups, lds, stream);
+    case 3: return launch_variant<false, true, true>(p, groups, lds, stream);
+    case 4: return launch_variant<true, false, false>(p, groups, lds, stream);
+    case 5: return launch_variant<true, false, true>(p, groups, lds, stream);
+    case 6: return launch_variant<true, true, false>(p, groups, lds, stream);
+    default: return launch_variant<true, true, true>(p, groups, lds, stream);
+  }
 }
 
 }  // namespace lcv

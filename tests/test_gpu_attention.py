@@ -85,13 +85,14 @@ def test_cached_matches_full_bitwise(lib, name, grid, heads, cond, local, stride
 
 def test_peaked_softmax(lib):
     """Q scaled by 8 (scores of standard deviation 8, up to ~40): exercises the running-max
-    rescaling.  This stress input is not one of the workloads, so its bound is derived
-    from the arithmetic: the rotated Q and K are rounded to bf16 (unit roundoff u = 2^-8)
-    before the matrix cores, which moves a score by about u*|q||k|/8/sqrt(2) ~ 0.02 here
-    (|q| ~ 64, |k| ~ 8) and up to ~0.5 in the worst case.  In a row dominated by two keys
-    this shifts their weights by a few percent, so an output element can move by a few
-    percent of |v_a - v_b| (~3): max-abs <= 0.1, while rel-L2 stays <= 1e-2 and the lse
-    moves by at most the score error (<= 0.05 here)."""
+    rescaling.  This stress input is not one of the workloads, so its bound is derived from
+    the arithmetic.  Each score sum_d q_d k_d / 8 sees three bf16 roundings before the matrix
+    cores (rotated Q, Q times log2(e)/8, rotated K; unit roundoff u = 2^-8 each): the score
+    error has standard deviation ~ u * sqrt(sum_d q_d^2 k_d^2) / 8 ~ 0.03 here (|q_d| ~ 8,
+    |k_d| ~ 1) and is at most 3u * |q||k| / 8 ~ 0.75.  The LSE moves by at most the largest
+    score error of its row (bound 0.25, about 8 standard deviations); in a row dominated by two
+    keys the output moves by a few percent of |v_a - v_b| (~3): max-abs <= 0.1, while the
+    relative L2 error stays <= 1e-2."""
     grid = (3, 10, 21)
     say("[attn] peaked softmax")
     _, (qb, kb, vb), _, out, lse = _run_full(lib, grid, 2, 210, 2, 4, seed=33, q_scale=8.0)
@@ -99,11 +100,11 @@ def test_peaked_softmax(lib):
                                       210, 2, 4)
     got = from_dev_f64(out)
     max_abs, rel = out_errors(got, ref_o)
-    say(f"  peaked: max_abs {max_abs:.3e} rel_l2 {rel:.3e}")
+    lse_err = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_l)))
+    say(f"  peaked: max_abs {max_abs:.3e} rel_l2 {rel:.3e} lse {lse_err:.3e}")
     assert np.all(np.isfinite(got))
     assert max_abs <= 0.1 and rel <= 1e-2, (max_abs, rel)
-    lse_err = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_l)))
-    assert lse_err <= 0.05, lse_err
+    assert lse_err <= 0.25, lse_err
 
 
 def test_batch_two(lib):
