@@ -14,14 +14,15 @@
 //    MFMA operands (RoPE applied once at load).
 //  * The workgroup walks the union of its query blocks' key-block rows (built with the
 //    layout, each entry carrying a per-wavefront membership mask).  Each K and V block
-//    (64 x 64 bf16) is staged once into LDS for all wavefronts: global -> VGPR prefetch of
-//    entry e+1 overlaps the MFMA/softmax work on entry e, then goes to the other LDS
-//    buffer (K RoPE applied on the way); one barrier per entry.
+//    (64 x 64 bf16) is staged once into LDS for all wavefronts by direct global -> LDS
+//    copies: block e+1 is copied into the other stage while block e is processed (K RoPE,
+//    when fused, goes through registers instead); one barrier per entry.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q as B), so
 //    each lane owns one query column: row statistics need only the partner lane l^32.
 //  * Online softmax in the log2 domain with a per-row reference max that only moves when a
-//    block's probabilities would exceed 2^8 (lazy rescaling): the common block costs one
-//    FMA, one v_exp_f32, half a conversion and half a dot2 per score.  Each row's decisions
+//    half block's probabilities grow too large (lazy rescaling).  The reference is
+//    subtracted inside the matrix-core product (one extra MFMA step), so the common score
+//    costs one v_exp_f32, half a conversion and half a dot2.  Each row's decisions
 //    depend on that row alone, so results do not depend on which other rows share the
 //    wavefront (the cached call reproduces the full call bit for bit).
 //  * O^T += V^T P^T with the same MFMA: P (bf16) comes straight from the S^T registers, V^T
@@ -50,10 +51,11 @@ constexpr int kThreads = 64 * kWaves;
 #endif
 constexpr int kWavesPerSimd = LCV_WAVES_PER_SIMD;  // occupancy the register budget is sized for
 constexpr int kTileBytes = 64 * 128;            // one 64 x 64 bf16 tile
-constexpr int kStageBytes = 2 * kTileBytes;     // K tile + V tile
-constexpr int kRopeTabOffset = 2 * kStageBytes; // two stages, then the cos/sin table
 constexpr float kScoreToLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-constexpr float kRescaleLimit = 256.0f;                     // lazy-rescale threshold 2^8
+// Lazy rescaling: a lane's probabilities in one 32-key half (16 keys of its row) may sum to
+// at most 2^7 before the row's reference max moves, so a row's half-block sum stays <= 2^8.
+// Testing each lane on its own keeps the partner exchange out of the common path.
+constexpr float kRescaleLimit = 128.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 
@@ -110,23 +112,23 @@ __device__ __forceinline__ const uint16_t* kv_row(const FwdParams& P, const uint
   return noise + ((int64_t)bh * (P.N - P.kv_split) + (key - P.kv_split)) * 64;
 }
 
-// Issue the asynchronous global -> LDS copies of block j into stage `stage` (V always, K
-// too unless K is rotated on the way); K chunks to be rotated are loaded into kreg.
+// Issue the asynchronous global -> LDS copies of block j into a stage's K and V tiles (V
+// always, K too unless K is rotated on the way); K chunks to be rotated are loaded into kreg.
 template <bool ROPE_K, bool CACHED>
-__device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* stage, int bh, int j, int wave,
-                                            int lane, u32x4 (&kreg)[kLoadsPerWave]) {
+__device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* kdst, unsigned char* vdst, int bh, int j,
+                                            int wave, int lane, u32x4 (&kreg)[kLoadsPerWave]) {
   const int gch = (lane & 7) ^ (lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
     const int key = 64 * j + 8 * u + (lane >> 3);
     const uint16_t* vsrc = kv_row<CACHED>(P, P.v_cond, P.v, bh, key) + 8 * gch;
-    __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(stage + kTileBytes + 1024 * u), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + 1024 * u), 16, 0, 0);
     const uint16_t* ksrc = kv_row<CACHED>(P, P.k_cond, P.k, bh, key) + 8 * gch;
     if constexpr (ROPE_K)
       kreg[c] = *reinterpret_cast<const u32x4*>(ksrc);
     else
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(stage + 1024 * u), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + 1024 * u), 16, 0, 0);
   }
 }
 
@@ -206,6 +208,14 @@ __device__ __forceinline__ u32x4 scale_chunk(u32x4 raw) {
 
 template <bool ROPE_Q, bool ROPE_K, bool CACHED>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const FwdParams P) {
+  // LDS: the K and V tiles of stages 0 and 1 are four separate variables, so the compiler
+  // can tell that reads of one stage do not depend on the global -> LDS copies into the
+  // other (with one shared array it makes those reads wait for every copy in flight); the
+  // dynamic part holds the cos/sin table.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   const int st = P.st_first + (item - bh * P.n_st_active);
 
   // ---- cos/sin table of every (axis, position, pair) of the grid
-  float2* tab = reinterpret_cast<float2*>(smem + kRopeTabOffset);
+  float2* tab = reinterpret_cast<float2*>(smem);
   if constexpr (ROPE_Q || ROPE_K) {
     for (int e = tid; e < P.rope_entries; e += kThreads) {
       int pos, p, width;
@@ -299,19 +309,19 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   u32x4 kreg[kLoadsPerWave];
   if (cnt > 0) {
     const int j0 = ents[0] >> 8;
-    stage_issue<ROPE_K, CACHED>(P, smem, bh, j0, wave, lane, kreg);
-    if constexpr (ROPE_K) stage_store_k(P, smem, j0, wave, lane, tab, kreg);
+    stage_issue<ROPE_K, CACHED>(P, lds_k0, lds_v0, bh, j0, wave, lane, kreg);
+    if constexpr (ROPE_K) stage_store_k(P, lds_k0, j0, wave, lane, tab, kreg);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // S^T[key][query] - m = K Q'^T + (ones x -m) for the keys 32*kt .. 32*kt+31 of a stage
   auto qk_half = [&](auto stage_tag, int kt, f32x16 (&s)[2]) {
-    constexpr uint32_t SB = decltype(stage_tag)::value * kStageBytes;
+    const unsigned char* kb = decltype(stage_tag)::value ? lds_k1 : lds_k0;
     bf16x8 ka[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      ka[ks] = *reinterpret_cast<const bf16x8*>(smem + SB + ka_off[ks] + 4096u * kt);
+      ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       f32x16 acc;
@@ -338,7 +348,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   };
 
   // Online softmax of one half: p = 2^(s - m) with the row's reference m already folded into
-  // s.  The reference only moves when the row's probabilities in this half would exceed 2^8;
+  // s.  The reference only moves when a lane's probabilities in this half exceed the limit;
   // the fast path is then one v_exp_f32, half a conversion and half a dot2 per score.
   // Returns per query tile the change of the folded reference (0 when it did not move), which
   // the caller applies to scores that were formed with the previous reference.
@@ -346,8 +356,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       psum[qt] = probs<false>(s[qt], 0.f, pb[qt]);
-      const float row_sum = psum[qt] + partner(psum[qt]);
-      trig[qt] = (mref[qt] == -INFINITY) || !(row_sum <= kRescaleLimit);
+      trig[qt] = (mref[qt] == -INFINITY) || !(psum[qt] <= kRescaleLimit);
     }
   };
   auto softmax_slow = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float (&psum)[2], const bool (&trig)[2],
@@ -359,7 +368,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[qt][r]);
       bm = fmaxf(bm, partner(bm));
       const float m_fold = (mref[qt] == -INFINITY) ? 0.f : mref[qt];
-      const float m_new = trig[qt] ? fmaxf(mref[qt], bm + m_fold) : mref[qt];
+      // both lanes of a row take the row's decision (the exchange runs on all lanes: under
+      // a short-circuit || the triggered lanes would skip it and their partners would read
+      // an inactive lane)
+      const int partner_trig = __shfl_xor((int)trig[qt], 32, 64);
+      const bool row_trig = trig[qt] || partner_trig != 0;
+      const float m_new = row_trig ? fmaxf(mref[qt], bm + m_fold) : mref[qt];
       const float alpha = (m_new == mref[qt]) ? 1.f : __builtin_amdgcn_exp2f(mref[qt] - m_new);
       o[0][qt] *= alpha;
       o[1][qt] *= alpha;
@@ -375,16 +389,16 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   // O^T[d][query] += V^T P^T over the two 16-key steps of half kt; V^T operands by
   // transposing reads of the row-major V tile
   auto pv_half = [&](auto stage_tag, int kt, const bf16x8 (&pb)[2][2]) {
-    constexpr uint32_t SB = decltype(stage_tag)::value * kStageBytes;
+    const unsigned char* vb = decltype(stage_tag)::value ? lds_v1 : lds_v0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t js_off = 2048u * (2 * kt + h);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(smem + SB + kTileBytes + vb_off[dt] + js_off));
+            (lds_i16x4*)(vb + vb_off[dt] + js_off));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(smem + SB + kTileBytes + vb_off[dt] + js_off + 1024u));
+            (lds_i16x4*)(vb + vb_off[dt] + js_off + 1024u));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     int jn = 0;
     if (has_next) {
       jn = ents[e + 1] >> 8;
-      stage_issue<ROPE_K, CACHED>(P, smem + (1 - STAGE) * kStageBytes, bh, jn, wave, lane, kreg);
+      stage_issue<ROPE_K, CACHED>(P, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, bh, jn, wave, lane, kreg);
     }
     if (wave_on && ((ent >> wave) & 1)) {
       const int j = ent >> 8;
@@ -464,7 +478,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
         attend(stage_tag, std::false_type{}, j);
     }
     if constexpr (ROPE_K) {
-      if (has_next) stage_store_k(P, smem + (1 - STAGE) * kStageBytes, jn, wave, lane, tab, kreg);
+      if (has_next) stage_store_k(P, STAGE ? lds_k0 : lds_k1, jn, wave, lane, tab, kreg);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -514,7 +528,7 @@ hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.n_items == 0) return hipSuccess;
   const unsigned groups = (unsigned)(((int64_t)p.n_items + 7) / 8 * 8);
   const bool rq = (p.flags & LCV_ROPE_Q) != 0, rk = (p.flags & LCV_ROPE_K) != 0, cached = p.kv_split > 0;
-  const size_t lds = (size_t)kRopeTabOffset + ((rq || rk) ? (size_t)p.rope_entries * sizeof(float2) : 0);
+  const size_t lds = (rq || rk) ? (size_t)p.rope_entries * sizeof(float2) : 0;
   const int v = (rq ? 4 : 0) | (rk ? 2 : 0) | (cached ? 1 : 0);
   switch (v) {
     case 0: return launch_variant<false, false, false>(p, groups, lds, stream);
