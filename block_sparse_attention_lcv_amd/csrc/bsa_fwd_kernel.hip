@@ -16,7 +16,8 @@
 //    layout, each entry carrying a per-wavefront membership mask).  Each K and V block
 //    (64 x 64 bf16) is staged once into LDS for all wavefronts by direct global -> LDS
 //    copies: block e+1 is copied into the other stage while block e is processed (K RoPE,
-//    when fused, goes through registers instead); one barrier per entry.
+//    when fused, goes through registers instead); one barrier per entry.  Each SIMD runs
+//    two wavefronts of different workgroups, whose matrix-core and vector phases overlap.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q as B), so
 //    each lane owns one query column: row statistics need only the partner lane l^32.
 //  * Online softmax in the log2 domain with a per-row reference max that only moves when a
@@ -306,9 +307,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   const int32_t* ents = P.st_ent + P.row_ptr[st * kWaves];
   const int cnt = P.st_cnt[st];
 
+  // List entries are wave-uniform (SGPRs): entry e+1 is known when step e starts (its block
+  // is copied during step e) and entry e+2 is loaded during step e.
   u32x4 kreg[kLoadsPerWave];
+  int ent_cur = 0, ent_next = 0;
   if (cnt > 0) {
-    const int j0 = ents[0] >> 8;
+    ent_cur = __builtin_amdgcn_readfirstlane(ents[0]);
+    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(ents[1]);
+    const int j0 = ent_cur >> 8;
     stage_issue<ROPE_K, CACHED>(P, lds_k0, lds_v0, bh, j0, wave, lane, kreg);
     if constexpr (ROPE_K) stage_store_k(P, lds_k0, j0, wave, lane, tab, kreg);
   }
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   // interleaved instruction by instruction, so one wavefront keeps the matrix cores and the
   // vector ALU busy at the same time.  A rescale of the first half (rare) shifts the second
   // half's scores by the change of the folded reference.
-  auto attend = [&](auto stage_tag, auto mask_tag, int j) {
+  auto attend = [&](auto stage_tag, auto mask_tag, int j, auto&& copies) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = 64 * j;
     f32x16 s0[2], s1[2];
@@ -421,6 +427,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     bool trig[2];
     qk_half(stage_tag, 0, s0);
     if (MASK) mask_half(key0, 0, s0);
+    // the next block's copies go out under the first half's matrix-core work, so that the
+    // loads of all wavefronts do not queue up at the start of the step
+    copies();
     qk_half(stage_tag, 1, s1);
     softmax_fast(s0, p0, psum, trig);
     // 4 K reads, then 10 Q K^T MFMAs of the first half, then the second half's 10 MFMAs
@@ -461,27 +470,31 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 
   auto step = [&](auto stage_tag, int e) {
     constexpr int STAGE = decltype(stage_tag)::value;
-    const int ent = ents[e];
-    const bool has_next = e + 1 < cnt;
-    int jn = 0;
-    if (has_next) {
-      jn = ents[e + 1] >> 8;
+    const int ent = ent_cur;
+    const int jn = ent_next >> 8;
+    // copies of block e+1 into the other stage; past the end of the list they re-read block
+    // 0 into that stage, which nothing reads any more
+    auto copies = [&]() __attribute__((always_inline)) {
       stage_issue<ROPE_K, CACHED>(P, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, bh, jn, wave, lane, kreg);
-    }
+    };
+    // in flight until the barrier below (all lanes load the same entry)
+    const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
     if (wave_on && ((ent >> wave) & 1)) {
       const int j = ent >> 8;
       bool need_mask = 64 * j + 63 >= P.N;
       if constexpr (!CACHED) need_mask = need_mask || (64 * qblk < P.C && 64 * j + 63 >= P.C);
       if (need_mask)
-        attend(stage_tag, std::true_type{}, j);
+        attend(stage_tag, std::true_type{}, j, copies);
       else
-        attend(stage_tag, std::false_type{}, j);
+        attend(stage_tag, std::false_type{}, j, copies);
+    } else {
+      copies();
     }
-    if constexpr (ROPE_K) {
-      if (has_next) stage_store_k(P, STAGE ? lds_k0 : lds_k1, jn, wave, lane, tab, kreg);
-    }
+    if constexpr (ROPE_K) stage_store_k(P, STAGE ? lds_k0 : lds_k1, jn, wave, lane, tab, kreg);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    ent_cur = ent_next;
+    ent_next = __builtin_amdgcn_readfirstlane(ent_after_raw);
   };
 
   int e = 0;
