@@ -24,14 +24,18 @@ fusion or reordering beyond what that definition states:
   keys (k < C)  [myzaker article, section on technical principles: block attention
   with a KV cache keeps condition tokens unaffected by noise tokens];
 * softmax attention with scale 1/sqrt(64) and the natural-log LSE of the scaled scores;
-* the CSR of attended key blocks per query block.
+* the CSR of attended key blocks per query block;
+* the query/key prologue: RMSNorm over each head's 64 channels with a per-channel gain,
+  then the 3D-RoPE  [myzaker article, section on technical principles: RMSNorm in the
+  self-attention module, 3D RoPE on visual tokens].
 
 Readings taken where the pages are silent (each listed in the design notes): local is
 a radius; global blocks are key columns j % s == 0 (s == 0 disables them); blocks are
 64 consecutive tokens of the flattened (t, y, x) order; condition tokens are the first
 C tokens; noise rows attend by the layout alone; RoPE pairs are adjacent channels,
 integer positions from 0, theta = 1e4; attention is bidirectional; a row with no
-attended key yields out = 0 and lse = -inf.
+attended key yields out = 0 and lse = -inf; RMSNorm works per head over its 64 channels
+with one 64-value gain and is applied before the rotation.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to properties fixed
 by the pages or by mathematics; nothing here is unpinned.
@@ -83,6 +87,23 @@ def rope3d_at(x: np.ndarray, tokens: np.ndarray, grid, theta: float = 10000.0) -
 
 
 # --------------------------------------------------------------------------- layout
+def rmsnorm(x: np.ndarray, gamma, eps: float) -> np.ndarray:
+    """RMS normalisation over the channel (last) axis with a per-channel gain:
+    y = x / sqrt(mean(x**2) + eps) * gamma  [myzaker article, section on technical
+    principles: RMSNorm in the self-attention module].  Reading taken: it normalises each
+    head's 64 query or key channels on their own, with one gain vector of 64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    mean_sq = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(mean_sq + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def qk_norm_rope(x: np.ndarray, gamma, eps: float, grid, theta: float = 10000.0, token_offset: int = 0) -> np.ndarray:
+    """Query/key prologue of the self-attention: RMSNorm of each head's channels, then the
+    partitioned 3D-RoPE of the token's position (norm first, rotation second, as the
+    rotation acts on the normalised channels)."""
+    return rope3d(rmsnorm(x, gamma, eps), grid, theta, token_offset)
+
+
 def n_blocks_of(n_tokens: int) -> int:
     return -(-n_tokens // BLOCK)
 

@@ -107,6 +107,90 @@ def pin_rope_closed_form_first_pair(impl):
         assert abs(y[0, c0] - math.cos(3.0)) < 1e-15 and abs(y[0, c0 + 1] - math.sin(3.0)) < 1e-15
 
 
+# ----------------------------------------------------------------------------- QK prologue
+def _rms_fsum(row) -> float:
+    """Root mean square of one channel vector, summed with math.fsum."""
+    return math.sqrt(math.fsum(float(v) * float(v) for v in row) / len(row))
+
+
+def pin_rmsnorm_unit_rms(impl):
+    """With unit gains and eps = 0 every normalised token has root mean square 1 and keeps
+    its direction (myzaker article, technical principles: RMSNorm in self-attention)."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((5, 64)) * np.array([[0.01], [1.0], [3.0], [250.0], [1e-3]])
+    y = impl.rmsnorm(x, np.ones(64), 0.0)
+    for r in range(x.shape[0]):
+        assert abs(_rms_fsum(y[r]) - 1.0) < 1e-13
+        ratio = y[r] / x[r]
+        assert np.max(np.abs(ratio - ratio[0])) < 1e-12 * abs(ratio[0]) and ratio[0] > 0
+
+
+def pin_rmsnorm_scale_invariance(impl):
+    """eps = 0: rmsnorm(c x) = rmsnorm(x) for c > 0 and rmsnorm(-x) = -rmsnorm(x)."""
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((3, 64))
+    g = rng.uniform(0.5, 2.0, 64)
+    base = impl.rmsnorm(x, g, 0.0)
+    for c in (1e-3, 0.37, 12.0, 4096.0):
+        assert np.max(np.abs(impl.rmsnorm(c * x, g, 0.0) - base)) < 1e-12
+    assert np.max(np.abs(impl.rmsnorm(-x, g, 0.0) + base)) < 1e-13
+
+
+def pin_rmsnorm_closed_form(impl):
+    """Hand-computed case: x = (3, 4, 0, ..., 0) over 64 channels has mean square 25/64, so
+    with eps = 0 the unit-gain result is (4.8, 6.4, 0, ...); eps = 25/64 doubles the mean
+    square (divisor sqrt(50)/8); the gain multiplies channel by channel; a zero vector stays
+    zero when eps > 0."""
+    x = np.zeros((1, 64))
+    x[0, 0], x[0, 1] = 3.0, 4.0
+    y = impl.rmsnorm(x, np.ones(64), 0.0)
+    assert abs(y[0, 0] - 4.8) < 1e-14 and abs(y[0, 1] - 6.4) < 1e-14 and np.all(y[0, 2:] == 0.0)
+    y = impl.rmsnorm(x, np.ones(64), 25.0 / 64.0)
+    assert abs(y[0, 0] - 3.0 * 8.0 / math.sqrt(50.0)) < 1e-14 and abs(y[0, 1] - 4.0 * 8.0 / math.sqrt(50.0)) < 1e-14
+    g = np.arange(64, dtype=np.float64) + 0.5
+    y = impl.rmsnorm(x, g, 0.0)
+    assert abs(y[0, 0] - 4.8 * 0.5) < 1e-14 and abs(y[0, 1] - 6.4 * 1.5) < 1e-14
+    z = impl.rmsnorm(np.zeros((2, 64)), g, 1e-6)
+    assert np.all(z == 0.0)
+
+
+def pin_qk_prologue_textbook(impl):
+    """The prologue is RMSNorm (per token, gain applied channel by channel) followed by the
+    textbook rotation of every section: checked with an fsum root mean square and complex
+    rotations, on a non-uniform gain so that the order of the two steps matters."""
+    rng = np.random.default_rng(43)
+    grid = (3, 5, 7)
+    theta = 10000.0
+    off = 17   # rows are tokens off .. T*H*W-1, as for the noise rows of a cached call
+    n = grid[0] * grid[1] * grid[2] - off
+    x = rng.standard_normal((2, n, 64)) * 2.0
+    g = rng.uniform(0.25, 3.0, 64)
+    eps = 1e-5
+    y = impl.qk_norm_rope(x, g, eps, grid, theta, token_offset=off)
+    t, yy, xx = np.unravel_index(np.arange(off, off + n), grid)
+    for b in range(2):
+        inv = np.array([1.0 / math.sqrt(math.fsum(float(v) * float(v) for v in row) / 64.0 + eps) for row in x[b]])
+        nx = x[b] * inv[:, None] * g[None, :]
+        z = nx[:, 0::2] + 1j * nx[:, 1::2]
+        ref = np.concatenate([
+            _textbook_rope_1d(z[:, 0:8], t, 16, theta),
+            _textbook_rope_1d(z[:, 8:20], yy, 24, theta),
+            _textbook_rope_1d(z[:, 20:32], xx, 24, theta),
+        ], axis=1)
+        got = y[b][:, 0::2] + 1j * y[b][:, 1::2]
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def pin_qk_prologue_norm(impl):
+    """Unit gains, eps = 0: every output token has Euclidean norm sqrt(64) = 8 exactly (the
+    normalisation sets it, the rotation conserves it), at any token offset."""
+    rng = np.random.default_rng(44)
+    grid = (4, 6, 5)
+    x = rng.standard_normal((3, 40, 64)) * 7.0
+    y = impl.qk_norm_rope(x, np.ones(64), 0.0, grid, token_offset=60)
+    assert np.max(np.abs(np.linalg.norm(y, axis=-1) - 8.0)) < 1e-12
+
+
 # ----------------------------------------------------------------------------- layout
 def _brute_token_mask(n_tokens, cond_len, local, stride):
     """Token mask by pure-Python loops over every (q, k)."""
@@ -347,4 +431,6 @@ ALL_PINS = [
     pin_two_block_layouts, pin_nnz_closed_form, pin_attended_pairs_closed_form,
     pin_two_block_brute_force, pin_full_layout_is_dense_sdpa, pin_condition_isolation,
     pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_empty_row,
+    pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
+    pin_qk_prologue_norm,
 ]

@@ -42,6 +42,20 @@ MUTANTS = {
     "cached_kv_order": [("k_full = np.concatenate([np.asarray(k_cond, np.float64), np.asarray(k_noise, np.float64)], axis=2)",
                          "k_full = np.concatenate([np.asarray(k_noise, np.float64), np.asarray(k_cond, np.float64)], axis=2)")],
     "cached_q_positions": [("tokens = local_rows + cond_len", "tokens = local_rows")],
+    "rmsnorm_sum_not_mean": [("mean_sq = np.mean(x * x, axis=-1, keepdims=True)",
+                              "mean_sq = np.sum(x * x, axis=-1, keepdims=True)")],
+    "rmsnorm_no_sqrt": [("return x / np.sqrt(mean_sq + eps) * np.asarray(gamma, dtype=np.float64)",
+                         "return x / (mean_sq + eps) * np.asarray(gamma, dtype=np.float64)")],
+    "rmsnorm_eps_outside": [("return x / np.sqrt(mean_sq + eps) * np.asarray(gamma, dtype=np.float64)",
+                             "return x / (np.sqrt(mean_sq) + eps) * np.asarray(gamma, dtype=np.float64)")],
+    "rmsnorm_wrong_axis": [("mean_sq = np.mean(x * x, axis=-1, keepdims=True)",
+                            "mean_sq = np.mean(x * x, axis=0, keepdims=True)")],
+    "rmsnorm_gain_inside": [("x = np.asarray(x, dtype=np.float64)\n    mean_sq",
+                             "x = np.asarray(x, dtype=np.float64) * np.asarray(gamma, dtype=np.float64)\n    mean_sq")],
+    "prologue_rope_first": [("return rope3d(rmsnorm(x, gamma, eps), grid, theta, token_offset)",
+                             "return rmsnorm(rope3d(x, grid, theta, token_offset), gamma, eps)")],
+    "prologue_no_offset": [("return rope3d(rmsnorm(x, gamma, eps), grid, theta, token_offset)",
+                            "return rope3d(rmsnorm(x, gamma, eps), grid, theta, 0)")],
 }
 
 
