@@ -146,6 +146,50 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
                       f"(fp64 numpy oracle: RoPE + masked dense attention), {dt:.2f} s"}
 
 
+def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
+    """The QK prologue (RMSNorm of each head's channels + 3D-RoPE) on this workload's Q and
+    K, timed apart from the attention step: HBM-bound, algorithmic bytes = bf16 read + write
+    of every element (4 B per element per launch)."""
+    gen = torch.Generator(device="cpu").manual_seed(12)
+    gq = (torch.rand(64, generator=gen) + 0.5).cuda()
+    gk = (torch.rand(64, generator=gen) + 0.5).cuda()
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    for _ in range(3):
+        bsa.qk_rmsnorm_rope3d(q, gq, 1e-6, w.grid, out=qn)
+        bsa.qk_rmsnorm_rope3d(k, gk, 1e-6, w.grid, out=kn)
+    torch.cuda.synchronize()
+    # back-to-back launches between two events (per-launch events would add the host's
+    # launch latency whenever the queue runs dry)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        bsa.qk_rmsnorm_rope3d(q, gq, 1e-6, w.grid, out=qn)
+        bsa.qk_rmsnorm_rope3d(k, gk, 1e-6, w.grid, out=kn)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (2 * steps)
+    nbytes = 4.0 * q.numel()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    # a plain device copy of the same tensor: the HBM rate a read + write stream reaches here
+    for _ in range(3):
+        qn.copy_(q)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        qn.copy_(q)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = nbytes / (a.elapsed_time(b) / steps * 1e-3) / 1e9
+    log(f"[bench] QK prologue: {ms:.4f} ms per tensor, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBS:.1f}% of HBM; "
+        f"a plain copy of the tensor: {copy_gbps:.0f} GB/s)")
+    del qn, kn
+    return {"bound": "hbm", "kernel": "qk_prologue_kernel", "avg_launch_ms": round(ms, 4),
+            "bytes_per_launch": nbytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBS, 4), "launches": 2 * steps,
+            "copy_reference_gbs": round(copy_gbps, 1),
+            "what": "RMSNorm over each head's 64 channels with a 64-value gain, then 3D-RoPE, on Q and on K"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +201,8 @@ def main() -> int:
                          "inside the attention kernel (both timed); fused: Q and K rotated inside the "
                          "attention kernel; none: inputs taken as already rotated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true",
+                    help="skip the separate measurement of the QK prologue (RMSNorm + 3D-RoPE) kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
     ap.add_argument("--copy-calibration", action="store_true",
@@ -280,6 +326,8 @@ def main() -> int:
         },
         "rope_pass_ms": round(float(np.mean(rope_ms)), 4) if args.rope_mode == "k-pass" else None,
     }
+    if not args.no_prologue:
+        result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

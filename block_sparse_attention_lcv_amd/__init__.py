@@ -22,8 +22,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 
 # Every symbol include/lcv_bsa.h declares.
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
-            "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_bsa_forward", "lcv_bsa_forward_cached",
-            "lcv_last_error", "lcv_abi_version")
+            "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d", "lcv_bsa_forward",
+            "lcv_bsa_forward_cached", "lcv_last_error", "lcv_abi_version")
 
 
 class LayoutParams(ctypes.Structure):
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         "lcv_bsa_layout_copy_csr": (i32, [vp, vp, vp, vp]),
         "lcv_bsa_layout_destroy": (None, [vp]),
         "lcv_rope3d_apply": (i32, [vp, vp, i64, i32, i32, ctypes.POINTER(Rope3dGrid), vp]),
+        "lcv_qk_rmsnorm_rope3d": (i32, [vp, vp, vp, ctypes.c_float, i64, i32, i32, ctypes.POINTER(Rope3dGrid), vp]),
         "lcv_bsa_forward": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), vp, vp, vp]),
         "lcv_bsa_forward_cached": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid),
                                          vp, vp, vp]),
@@ -195,6 +196,26 @@ def rope3d_apply(x, grid, token_offset: int = 0, out=None, stream=None):
     n_outer = x.numel() // (64 * n_tokens) if n_tokens else 0
     _check(lib().lcv_rope3d_apply(_bf16(x, "x"), _bf16(y, "out"), n_outer, n_tokens, token_offset,
                                   ctypes.byref(g.c()), _stream_ptr(stream)))
+    return y
+
+
+def qk_rmsnorm_rope3d(x, gamma, eps: float = 1e-6, grid=None, token_offset: int = 0, out=None, stream=None):
+    """RMSNorm of each 64-channel row of x[..., n_tokens, 64] (bf16) with the gain gamma[64]
+    (float32 CUDA tensor), then the 3D-RoPE when grid is given; out may be x."""
+    import torch
+    g = _as_grid(grid)
+    if x.shape[-1] != 64:
+        raise ValueError("last dimension must be 64")
+    if gamma.dtype != torch.float32 or not gamma.is_cuda or not gamma.is_contiguous() or gamma.numel() != 64:
+        raise ValueError("gamma must be a contiguous float32 CUDA tensor of 64 values")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    n_tokens = x.shape[-2]
+    n_outer = x.numel() // (64 * n_tokens) if n_tokens else 0
+    _check(lib().lcv_qk_rmsnorm_rope3d(_bf16(x, "x"), _bf16(y, "out"), gamma.data_ptr(), float(eps), n_outer,
+                                       n_tokens, token_offset, ctypes.byref(g.c()) if g is not None else None,
+                                       _stream_ptr(stream)))
     return y
 
 

@@ -321,10 +321,37 @@ lcv_status lcv_rope3d_apply(const void* x, void* y, int64_t n_outer, int32_t n_t
   if ((int64_t)token_offset + n_tokens > total)
     return fail(LCV_ERR_SHAPE, "tokens [%d, %lld) exceed the grid's %lld tokens", token_offset,
                 (long long)token_offset + n_tokens, (long long)total);
-  if (n_outer > (int64_t)65535 * 8) return fail(LCV_ERR_UNSUPPORTED, "n_outer above 524280 is not supported");
+  if (n_outer > (int64_t)65535 * 2) return fail(LCV_ERR_UNSUPPORTED, "n_outer above 131070 is not supported");
   const hipError_t e = lcv::launch_rope3d(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), n_outer, n_tokens,
                                           token_offset, grid->H, grid->W, std::log2(grid->theta), stream);
   if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+  return ok();
+}
+
+lcv_status lcv_qk_rmsnorm_rope3d(const void* x, void* y, const float* gamma, float eps, int64_t n_outer,
+                                 int32_t n_tokens, int32_t token_offset, const lcv_rope3d_grid* grid,
+                                 hipStream_t stream) {
+  if (x == nullptr || y == nullptr || gamma == nullptr) return fail(LCV_ERR_NULL, "x, y and gamma are required");
+  if (n_outer < 0 || n_tokens < 0 || token_offset < 0)
+    return fail(LCV_ERR_INVALID_ARG, "n_outer, n_tokens and token_offset must be >= 0");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(LCV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(LCV_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if (!aligned(gamma, 4)) return fail(LCV_ERR_INVALID_ARG, "gamma must be 4-byte aligned");
+  if (grid != nullptr) {
+    lcv_status st = check_grid(grid);
+    if (st != LCV_OK) return st;
+    const int64_t total = (int64_t)grid->T * grid->H * grid->W;
+    if ((int64_t)token_offset + n_tokens > total)
+      return fail(LCV_ERR_SHAPE, "tokens [%d, %lld) exceed the grid's %lld tokens", token_offset,
+                  (long long)token_offset + n_tokens, (long long)total);
+  } else if ((int64_t)token_offset + n_tokens >= (int64_t(1) << 31)) {
+    return fail(LCV_ERR_UNSUPPORTED, "token_offset + n_tokens must be below 2^31");
+  }
+  if (n_outer > (int64_t)65535 * 2) return fail(LCV_ERR_UNSUPPORTED, "n_outer above 131070 is not supported");
+  const hipError_t e = lcv::launch_qk_prologue(
+      static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), gamma, eps, n_outer, n_tokens, token_offset,
+      grid != nullptr, grid ? grid->H : 1, grid ? grid->W : 1, grid ? std::log2(grid->theta) : 0.f, stream);
+  if (e != hipSuccess) return hip_fail(e, "qk prologue launch");
   return ok();
 }
 

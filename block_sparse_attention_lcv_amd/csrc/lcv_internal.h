@@ -151,5 +151,8 @@ hipError_t launch_layout_build(const LayoutRule& L, const LayoutDev& d, hipStrea
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int64_t n_outer, int32_t n_tokens,
                          int32_t token_offset, int32_t H, int32_t W, float log2_theta, hipStream_t stream);
 hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_qk_prologue(const uint16_t* x, uint16_t* y, const float* gamma, float eps, int64_t n_outer,
+                              int32_t n_tokens, int32_t token_offset, bool rope, int32_t H, int32_t W,
+                              float log2_theta, hipStream_t stream);
 
 }  // namespace lcv

@@ -11,7 +11,7 @@ namespace lcv {
 namespace {
 
 constexpr int kRopeThreads = 256;
-constexpr int kRopeOuterPerThread = 8;
+constexpr int kRopeOuterPerThread = 2;
 
 __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(const uint16_t* x, uint16_t* y,
                                                              int64_t n_outer, int32_t n_tokens, int32_t token_offset,
@@ -32,14 +32,22 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(const uint16_t* x,
 #pragma unroll
   for (int e = 0; e < 4; ++e) cs[e] = rope_cos_sin(pos, p0 + e, width, log2_theta);
 
+  // the thread's chunks of its (up to) kRopeOuterPerThread slices are all loaded before any
+  // is used, so each thread keeps that many 16-byte loads in flight
   const int64_t o0 = (int64_t)blockIdx.y * kRopeOuterPerThread;
-  const int64_t o1 = (o0 + kRopeOuterPerThread < n_outer) ? o0 + kRopeOuterPerThread : n_outer;
-  for (int64_t o = o0; o < o1; ++o) {
-    const int64_t off = (o * n_tokens + tok) * 64 + 8 * c;
-    u32x4 w = *reinterpret_cast<const u32x4*>(x + off);
+  const int n_o = (int)((o0 + kRopeOuterPerThread < n_outer) ? kRopeOuterPerThread : n_outer - o0);
+  u32x4 w[kRopeOuterPerThread];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = rotate_pair(w[e], cs[e]);
-    *reinterpret_cast<u32x4*>(y + off) = w;
+  for (int i = 0; i < kRopeOuterPerThread; ++i) {
+    const int64_t o = o0 + (i < n_o ? i : n_o - 1);   // past the last slice: reload it (unused)
+    w[i] = *reinterpret_cast<const u32x4*>(x + (o * n_tokens + tok) * 64 + 8 * c);
+  }
+#pragma unroll
+  for (int i = 0; i < kRopeOuterPerThread; ++i) {
+    if (i >= n_o) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[i][e] = rotate_pair(w[i][e], cs[e]);
+    *reinterpret_cast<u32x4*>(y + ((o0 + i) * n_tokens + tok) * 64 + 8 * c) = w[i];
   }
 }
 

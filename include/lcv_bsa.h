@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 1
+#define LCV_BSA_ABI_VERSION 2
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -134,9 +134,25 @@ void lcv_bsa_layout_destroy(lcv_bsa_layout* layout);
  * slices (batch * heads) is token token_offset + r of the grid, so noise tokens of a cached
  * call pass token_offset = cond_len.  Math in fp32, result rounded to nearest even bf16.
  * Errors: NULL, INVALID_ARG (n_outer < 0, n_tokens < 0, token_offset < 0, theta <= 0,
- * misalignment), SHAPE (token_offset + n_tokens > T*H*W), HIP. */
+ * misalignment), SHAPE (token_offset + n_tokens > T*H*W), UNSUPPORTED (n_outer > 131070),
+ * HIP. */
 lcv_status lcv_rope3d_apply(const void* x, void* y, int64_t n_outer, int32_t n_tokens,
                             int32_t token_offset, const lcv_rope3d_grid* grid, hipStream_t stream);
+
+/* Query/key prologue of the self-attention (myzaker article, technical principles: RMSNorm
+ * in the self-attention module, 3D RoPE on visual tokens).  Each 64-channel row of
+ * x[n_outer, n_tokens, 64] (bf16) is RMS-normalised with the gain gamma[64] (fp32, device
+ * memory): x / sqrt(mean(x^2) + eps) * gamma; when grid is not NULL the partitioned 3D-RoPE
+ * then turns it by the position of token token_offset + r (row r of every slice).  The
+ * result goes to y (bf16; y may equal x, otherwise the two must not overlap).  Math in fp32,
+ * one rounding to nearest-even bf16 at the end.  Call it once for Q and once for K (each
+ * with its own gain) before lcv_bsa_forward with flags = 0.  Errors: NULL (x, y or gamma),
+ * INVALID_ARG (n_outer, n_tokens or token_offset < 0, eps < 0 or not finite, theta <= 0,
+ * x or y not 16-byte aligned, gamma not 4-byte aligned), SHAPE (token_offset + n_tokens >
+ * T*H*W), UNSUPPORTED (n_outer > 131070), HIP. */
+lcv_status lcv_qk_rmsnorm_rope3d(const void* x, void* y, const float* gamma, float eps, int64_t n_outer,
+                                 int32_t n_tokens, int32_t token_offset, const lcv_rope3d_grid* grid,
+                                 hipStream_t stream);
 
 /* Block-sparse attention over all N tokens.
  *   q, k, v : bf16 [batch, heads, N, 64], N = layout n_tokens

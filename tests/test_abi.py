@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 1
+    assert bsa.lib().lcv_abi_version() == 2
 
 
 QUERY_CASES = [
@@ -116,3 +116,25 @@ def test_rope_argument_errors():
     assert L.lcv_rope3d_apply(p, p, 1, 64, 0, ctypes.byref(bad_theta), None) == 2
     bad_dims = bsa.Rope3dGrid(0, 4, 8, 1e4)
     assert L.lcv_rope3d_apply(p, p, 1, 64, 0, ctypes.byref(bad_dims), None) == 2
+
+
+def test_qk_prologue_argument_errors():
+    L = bsa.lib()
+    g = bsa.Rope3dGrid(2, 4, 8, 1e4)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4098)
+    f = L.lcv_qk_rmsnorm_rope3d
+    assert f(None, p, p, 1e-6, 1, 64, 0, ctypes.byref(g), None) == 1
+    assert f(p, None, p, 1e-6, 1, 64, 0, ctypes.byref(g), None) == 1
+    assert f(p, p, None, 1e-6, 1, 64, 0, ctypes.byref(g), None) == 1
+    assert f(mis, p, p, 1e-6, 1, 64, 0, ctypes.byref(g), None) == 2
+    assert f(p, p, ctypes.c_void_p(4097), 1e-6, 1, 64, 0, ctypes.byref(g), None) == 2
+    assert f(p, p, p, -1e-6, 1, 64, 0, ctypes.byref(g), None) == 2
+    assert f(p, p, p, float("nan"), 1, 64, 0, ctypes.byref(g), None) == 2
+    assert f(p, p, p, 1e-6, -1, 64, 0, ctypes.byref(g), None) == 2
+    assert f(p, p, p, 1e-6, 1, 64, 1, ctypes.byref(g), None) == 3       # 65 tokens > 64
+    bad_theta = bsa.Rope3dGrid(2, 4, 8, 0.0)
+    assert f(p, p, p, 1e-6, 1, 64, 0, ctypes.byref(bad_theta), None) == 2
+    assert f(p, p, p, 1e-6, 600000, 64, 0, None, None) == 6
+    for code in (1, 2, 3, 6):
+        assert L.lcv_last_error()
