@@ -27,7 +27,11 @@ fusion or reordering beyond what that definition states:
 * the CSR of attended key blocks per query block;
 * the query/key prologue: RMSNorm over each head's 64 channels with a per-channel gain,
   then the 3D-RoPE  [myzaker article, section on technical principles: RMSNorm in the
-  self-attention module, 3D RoPE on visual tokens].
+  self-attention module, 3D RoPE on visual tokens];
+* the gradients of the attention with respect to q, k, v (the backward pass that LoRA
+  training of the model needs  [myzaker article, technical principles: the LoRA-trained
+  refinement expert; SimpleTuner quickstart "LongCat-Video Edit", LoRA training]) by the
+  chain rule through the row softmax.
 
 Readings taken where the pages are silent (each listed in the design notes): local is
 a radius; global blocks are key columns j % s == 0 (s == 0 disables them); blocks are
@@ -189,6 +193,43 @@ def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarr
     out[empty] = 0.0
     lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
     return out, lse
+
+
+def masked_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, dout: np.ndarray):
+    """Gradients of out = softmax(mask(q k^T / 8)) v with respect to q, k and v for the
+    upstream gradient dout[R,64] (fp64), by the chain rule through the softmax:
+    P = row softmax, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+    dQ = dS K / 8, dK = dS^T Q / 8.  Rows with an empty mask contribute nothing."""
+    s = (q @ k.T) * SOFTMAX_SCALE
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    p = e / np.where(empty, 1.0, l)[:, None]
+    p[empty] = 0.0
+    out = p @ v
+    dv = p.T @ dout
+    dp = dout @ v.T
+    delta = np.sum(dout * out, axis=1)
+    ds = p * (dp - delta[:, None])
+    dq = (ds @ k) * SOFTMAX_SCALE
+    dk = (ds.T @ q) * SOFTMAX_SCALE
+    return dq, dk, dv
+
+
+def bsa_backward(q, k, v, dout, cond_len: int, local: int, stride: int):
+    """Gradients dq, dk, dv [B, H, N, 64] of the block-sparse attention (no RoPE: q and k as
+    they enter the scores, i.e. already rotated) for the upstream gradient dout."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    bsz, heads, n_tokens, _ = q.shape
+    mask = token_mask_rows(np.arange(n_tokens), n_tokens, cond_len, local, stride)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(bsz):
+        for h in range(heads):
+            dq[b, h], dk[b, h], dv[b, h] = masked_attention_backward(q[b, h], k[b, h], v[b, h], mask, dout[b, h])
+    return dq, dk, dv
 
 
 def bsa_forward(q, k, v, grid, cond_len: int, local: int, stride: int, theta: float = 10000.0,

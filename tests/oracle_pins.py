@@ -425,6 +425,68 @@ def pin_empty_row(impl):
     assert np.allclose(out[1], 1.0) and abs(lse[1] - 8.0) < 1e-12
 
 
+# ----------------------------------------------------------------------------- backward
+def _bwd_case(seed, n_tokens=150, cond_len=70, heads=1):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((1, heads, n_tokens, 64)) for _ in range(4))
+    return q, k, v, do, cond_len
+
+
+def pin_backward_finite_differences(impl):
+    """The gradients are the derivatives of L = sum(dout * out): central differences of the
+    forward (step 1e-5, fp64) on sampled coordinates of q, k and v, on a layout with three
+    blocks, a partial last block and the condition rule (C = 70)."""
+    q, k, v, do, cond = _bwd_case(51)
+    grid = (1, 10, 15)
+    local, stride = 1, 2
+
+    def loss(qq, kk, vv):
+        out, _ = impl.bsa_forward(qq, kk, vv, grid, cond, local, stride, rope_q=False, rope_k=False)
+        return math.fsum((out * do).ravel())
+
+    dq, dk, dv = impl.bsa_backward(q, k, v, do, cond, local, stride)
+    rng = np.random.default_rng(52)
+    h = 1e-5
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(12):
+            t, c = int(rng.integers(0, q.shape[2])), int(rng.integers(0, 64))
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][0, 0, t, c] += h
+            lp = loss(*args)
+            args[which][0, 0, t, c] -= 2 * h
+            lm = loss(*args)
+            num = (lp - lm) / (2 * h)
+            assert abs(num - grad[0, 0, t, c]) < 1e-6 * max(1.0, abs(num)), (which, t, c, num, grad[0, 0, t, c])
+
+
+def pin_backward_sums(impl):
+    """Softmax is invariant to a shift of every key by one vector, so the key gradients of a
+    head sum to zero; the value gradients sum to the sum of dout over the non-empty rows
+    (each probability row sums to one)."""
+    q, k, v, do, cond = _bwd_case(53, n_tokens=200, cond_len=64, heads=2)
+    dq, dk, dv = impl.bsa_backward(q, k, v, do, cond, 2, 3)
+    for h in range(2):
+        assert np.max(np.abs(dk[0, h].sum(axis=0))) < 1e-10
+        assert np.max(np.abs(dv[0, h].sum(axis=0) - do[0, h].sum(axis=0))) < 1e-10
+
+
+def pin_backward_uniform_closed_form(impl):
+    """q = 0 gives uniform probabilities over each row's allowed keys: dv[key] is the sum of
+    dout[q] / (allowed count of q) over the rows q that see the key (brute-force loops)."""
+    rng = np.random.default_rng(54)
+    n, cond = 130, 64
+    q = np.zeros((1, 1, n, 64))
+    k, v, do = (rng.standard_normal((1, 1, n, 64)) for _ in range(3))
+    _, _, dv = impl.bsa_backward(q, k, v, do, cond, 0, 0)
+    allowed = _brute_token_mask(n, cond, 0, 0)
+    ref = np.zeros((n, 64))
+    for qi in range(n):
+        keys = [kj for kj in range(n) if allowed[qi][kj]]
+        for kj in keys:
+            ref[kj] += do[0, 0, qi] / len(keys)
+    assert np.max(np.abs(dv[0, 0] - ref)) < 1e-12
+
+
 ALL_PINS = [
     pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
@@ -432,5 +494,5 @@ ALL_PINS = [
     pin_two_block_brute_force, pin_full_layout_is_dense_sdpa, pin_condition_isolation,
     pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_empty_row,
     pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
-    pin_qk_prologue_norm,
+    pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
 ]

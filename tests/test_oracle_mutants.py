@@ -56,6 +56,13 @@ MUTANTS = {
                              "return rmsnorm(rope3d(x, grid, theta, token_offset), gamma, eps)")],
     "prologue_no_offset": [("return rope3d(rmsnorm(x, gamma, eps), grid, theta, token_offset)",
                             "return rope3d(rmsnorm(x, gamma, eps), grid, theta, 0)")],
+    "bwd_delta_sign": [("ds = p * (dp - delta[:, None])", "ds = p * (dp + delta[:, None])")],
+    "bwd_delta_dropped": [("ds = p * (dp - delta[:, None])", "ds = p * dp")],
+    "bwd_dq_scale": [("dq = (ds @ k) * SOFTMAX_SCALE", "dq = ds @ k")],
+    "bwd_dk_uses_k": [("dk = (ds.T @ q) * SOFTMAX_SCALE", "dk = (ds.T @ k) * SOFTMAX_SCALE")],
+    "bwd_dv_no_transpose": [("dv = p.T @ dout", "dv = p @ dout")],
+    "bwd_dp_uses_q": [("dp = dout @ v.T", "dp = dout @ q.T")],
+    "bwd_unnormalised_p": [("p = e / np.where(empty, 1.0, l)[:, None]", "p = e")],
 }
 
 
