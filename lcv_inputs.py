@@ -108,6 +108,13 @@ def qkv_bits(seed: int, batch: int, heads: int, n_tokens: int, q_scale: float = 
     return q, k, v
 
 
+def grad_bits(seed: int, batch: int, heads: int, n_tokens: int) -> np.ndarray:
+    """Upstream gradient dO of the attention output as bf16 bit patterns [batch, heads,
+    n_tokens, 64]: i.i.d. N(0,1) from its own PCG64 stream (seed + 10000)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 10000))
+    return normal_bf16(rng, (batch, heads, n_tokens, HEAD_DIM))
+
+
 def workload_inputs(w: Workload, call: int = 0, q_scale: float = 1.0):
     """Inputs of a workload.  call 0: full Q/K/V over all N tokens.  call 1 (cached
     workloads): fresh noise-token Q/K/V over the N-C noise tokens, seed + 100."""

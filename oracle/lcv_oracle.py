@@ -123,10 +123,15 @@ def block_mask(n_blocks: int, local: int, stride: int) -> np.ndarray:
 
 
 def token_mask_rows(rows: np.ndarray, n_tokens: int, cond_len: int, local: int, stride: int) -> np.ndarray:
-    """M[q, k] for the query tokens in ``rows`` and every key k < N:
+    """M[q, k] for the query tokens in ``rows`` and every key k < N."""
+    return token_mask(rows, np.arange(n_tokens), cond_len, local, stride)
+
+
+def token_mask(rows: np.ndarray, keys: np.ndarray, cond_len: int, local: int, stride: int) -> np.ndarray:
+    """M[q, k] for the query tokens in ``rows`` and the key tokens in ``keys``:
     the block mask of (q // 64, k // 64) and the condition rule (q >= C or k < C)."""
     rows = np.asarray(rows, dtype=np.int64)
-    keys = np.arange(n_tokens, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
     qi = rows // BLOCK
     kj = keys // BLOCK
     i = qi[:, None]
@@ -230,6 +235,42 @@ def bsa_backward(q, k, v, dout, cond_len: int, local: int, stride: int):
         for h in range(heads):
             dq[b, h], dk[b, h], dv[b, h] = masked_attention_backward(q[b, h], k[b, h], v[b, h], mask, dout[b, h])
     return dq, dk, dv
+
+
+def bsa_backward_rows(q, k, v, dout, cond_len: int, local: int, stride: int, rows):
+    """dq [B, H, R, 64] at the query tokens ``rows`` only: a row's dq depends on its own
+    softmax row alone, so the chain rule runs on those rows."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    rows = np.asarray(rows, dtype=np.int64)
+    bsz, heads, n_tokens, _ = q.shape
+    mask = token_mask_rows(rows, n_tokens, cond_len, local, stride)
+    dq = np.zeros((bsz, heads, rows.size, HEAD_DIM))
+    for b in range(bsz):
+        for h in range(heads):
+            dq[b, h] = masked_attention_backward(q[b, h, rows], k[b, h], v[b, h], mask, dout[b, h, rows])[0]
+    return dq
+
+
+def bsa_backward_keys(q, k, v, dout, cond_len: int, local: int, stride: int, keys, row_chunk: int = 512):
+    """dk, dv [B, H, K, 64] at the key tokens ``keys`` only: dk and dv of a key are sums over
+    the query rows that attend to it, so the chain rule runs on those rows (in chunks of
+    ``row_chunk``, whose contributions add)."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    keys = np.asarray(keys, dtype=np.int64)
+    bsz, heads, n_tokens, _ = q.shape
+    seen = token_mask(np.arange(n_tokens), keys, cond_len, local, stride).any(axis=1)
+    rows = np.nonzero(seen)[0]
+    dk = np.zeros((bsz, heads, keys.size, HEAD_DIM))
+    dv = np.zeros((bsz, heads, keys.size, HEAD_DIM))
+    for r0 in range(0, rows.size, row_chunk):
+        part = rows[r0:r0 + row_chunk]
+        mask = token_mask_rows(part, n_tokens, cond_len, local, stride)
+        for b in range(bsz):
+            for h in range(heads):
+                _, dkp, dvp = masked_attention_backward(q[b, h, part], k[b, h], v[b, h], mask, dout[b, h, part])
+                dk[b, h] += dkp[keys]
+                dv[b, h] += dvp[keys]
+    return dk, dv
 
 
 def bsa_forward(q, k, v, grid, cond_len: int, local: int, stride: int, theta: float = 10000.0,

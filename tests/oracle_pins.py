@@ -487,6 +487,24 @@ def pin_backward_uniform_closed_form(impl):
     assert np.max(np.abs(dv[0, 0] - ref)) < 1e-12
 
 
+def pin_backward_sampled_match_full(impl):
+    """dq at sampled rows and dk, dv at sampled keys (global, local-only, condition and last
+    partial-block keys; row chunks smaller than a block) equal the full backward; the key
+    subset's token mask equals the brute-force loops."""
+    q, k, v, do, cond = _bwd_case(55, n_tokens=300, cond_len=100, heads=2)
+    local, stride = 1, 3
+    dq, dk, dv = impl.bsa_backward(q, k, v, do, cond, local, stride)
+    rows = np.array([0, 63, 64, 99, 100, 180, 299])
+    keys = np.array([0, 5, 64, 99, 100, 130, 192, 250, 299])
+    assert np.allclose(impl.bsa_backward_rows(q, k, v, do, cond, local, stride, rows), dq[:, :, rows],
+                       rtol=0, atol=1e-12)
+    dks, dvs = impl.bsa_backward_keys(q, k, v, do, cond, local, stride, keys, row_chunk=37)
+    assert np.allclose(dks, dk[:, :, keys], rtol=0, atol=1e-12)
+    assert np.allclose(dvs, dv[:, :, keys], rtol=0, atol=1e-12)
+    allowed = np.array(_brute_token_mask(300, cond, local, stride))
+    assert np.array_equal(impl.token_mask(rows, keys, cond, local, stride), allowed[np.ix_(rows, keys)])
+
+
 ALL_PINS = [
     pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
@@ -495,4 +513,5 @@ ALL_PINS = [
     pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_empty_row,
     pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
+    pin_backward_sampled_match_full,
 ]
