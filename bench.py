@@ -190,6 +190,39 @@ def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
             "what": "RMSNorm over each head's 64 channels with a 64-value gain, then 3D-RoPE, on Q and on K"}
 
 
+def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: int, stream) -> dict:
+    """The attention backward (dQ, dK, dV from the forward's output and LSE) on this
+    workload, timed apart from the forward step (q and k taken as already rotated).
+    Effective rate by the usual convention: 2.5x the forward's FLOPs (five products of the
+    attended pairs: S, dP, dV, dQ, dK); the kernels execute seven (S and dP are formed once
+    for the query walk and once for the key walk), also reported."""
+    out, lse = bsa.forward(q, k, v, layout, grid=None)
+    gen = torch.Generator(device="cpu").manual_seed(13)
+    do = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(2 * q.shape[0] * q.shape[1] * q.shape[2], dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        bsa.backward(q, k, v, out, lse, do, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        bsa.backward(q, k, v, out, lse, do, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    eff = 2.5 * fwd_flops / (ms * 1e-3) / 1e12
+    executed = 3.5 * fwd_flops / (ms * 1e-3) / 1e12
+    log(f"[bench] backward: {ms:.3f} ms, {eff:.1f} TFLOP/s effective (2.5x forward FLOPs), "
+        f"{executed:.1f} TFLOP/s of executed matrix work")
+    del out, lse, do, dq, dk, dv, ws
+    return {"bound": "mfma", "kernels": ["bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"],
+            "ms": round(ms, 4), "effective_flops": 2.5 * fwd_flops, "achieved": round(eff, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / MFMA_BF16_PEAK_TFLOPS, 4),
+            "executed_tflops": round(executed, 3), "launches": steps,
+            "what": "dQ, dK, dV of the block-sparse attention (D = rowsum(dO*O) pass, query walk, key walk)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +236,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip the separate measurement of the QK prologue (RMSNorm + 3D-RoPE) kernel")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the separate measurement of the attention backward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
     ap.add_argument("--copy-calibration", action="store_true",
@@ -328,6 +363,8 @@ def main() -> int:
     }
     if not args.no_prologue:
         result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
+    if not args.no_backward:
+        result["backward"] = measure_backward(bsa, torch, q, k, v, layout, w, flops, args.steps, stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 # Every symbol include/lcv_bsa.h declares.
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
             "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d", "lcv_bsa_forward",
-            "lcv_bsa_forward_cached", "lcv_last_error", "lcv_abi_version")
+            "lcv_bsa_forward_cached", "lcv_bsa_backward", "lcv_last_error", "lcv_abi_version")
 
 
 class LayoutParams(ctypes.Structure):
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "lcv_bsa_forward": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), vp, vp, vp]),
         "lcv_bsa_forward_cached": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid),
                                          vp, vp, vp]),
+        "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp]),
         "lcv_last_error": (ctypes.c_char_p, []),
         "lcv_abi_version": (i32, []),
     }
@@ -267,3 +268,31 @@ def forward_cached(q_noise, k_noise, v_noise, k_cond, v_cond, layout: Layout, gr
                                         ctypes.byref(g.c()) if g is not None else None, _bf16(out, "out"),
                                         lse_ptr, _stream_ptr(stream)))
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, layout: Layout, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the block-sparse attention for the upstream gradient dout.
+    q, k as they entered the scores (rotated), out and lse [B, H, N] (float32) from forward."""
+    import torch
+    B, Hh, N, D = q.shape
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q [B, H, N, 64]")
+    if D != 64 or N != layout.n_tokens:
+        raise ValueError(f"q must be [B, H, {layout.n_tokens}, 64]")
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or lse.shape != (B, Hh, N):
+        raise ValueError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if workspace is None:
+        workspace = torch.empty(2 * B * Hh * N, dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda or workspace.numel() < 2 * B * Hh * N:
+        raise ValueError("workspace must be a float32 CUDA tensor of at least 2 * B * H * N values")
+    _check(lib().lcv_bsa_backward(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(out, "out"), lse.data_ptr(),
+                                  _bf16(dout, "dout"), B, Hh, layout.handle, layout.cond_len, _bf16(dq, "dq"),
+                                  _bf16(dk, "dk"), _bf16(dv, "dv"), workspace.data_ptr(), _stream_ptr(stream)))
+    return dq, dk, dv

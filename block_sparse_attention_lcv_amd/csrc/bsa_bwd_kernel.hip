@@ -1,0 +1,497 @@
+// Block-sparse 3D self-attention backward for gfx950 (MI355X): dQ, dK, dV of the attention
+// from the forward's output and LSE, for LoRA training of the model (myzaker article,
+// technical principles: the LoRA-trained refinement expert; SimpleTuner quickstart
+// "LongCat-Video Edit").  Inputs are Q and K as they entered the scores (already rotated).
+//
+// With P = exp(S - lse) recomputed from the saved LSE, the gradients are
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D) with D = rowsum(dO * O),
+//   dQ = dS K / 8, dK = dS^T Q / 8.
+// Three kernels:
+//  * bwd_prep_kernel: D and 8 * lse per row (HBM-bound, one pass over O and dO);
+//  * bwd_dq_kernel: the row walk of the forward -- a workgroup of 8 wavefronts owns 4 query
+//    blocks (32 rows per wavefront) and streams the K and V blocks of their rows through LDS;
+//    per 32-key half it forms S^T = K Q^T and dP^T = V dO^T with v_mfma_f32_32x32x16_bf16
+//    (8 * lse and D folded into one extra MFMA step each, as the forward folds its row max),
+//    then dS^T and dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16;
+//  * bwd_dkdv_kernel: the column walk -- a workgroup owns 4 key blocks (32 keys per
+//    wavefront) grouped so that their columns nearly coincide (the strided global blocks
+//    together) and streams the Q and dO blocks, lse and D of the union of their columns;
+//    S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+// Scores stay unscaled dot products of the bf16 inputs (exact products, fp32 sums); the row's
+// 8 * lse is subtracted before the one multiply by log2(e)/8 that feeds exp2.
+// Every output row is written by exactly one wavefront, with no atomics: results are
+// deterministic.
+#include <type_traits>
+
+#include "lcv_internal.h"
+#include "rope_math.h"
+
+namespace lcv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBwdWaves = 2 * kWaves;         // two wavefronts (32 rows each) per 64-row block
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kTileBytes = 64 * 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kScoreToLog2 = kLog2e / 8.0f;
+constexpr float kEmptyRowLse8 = 3.0e38f;      // 8 * lse of a row with no key: p = 0
+static_assert(kBwdWaves == 8, "a 64 x 64 tile is 8 wave-loads of 1 KB, one per wavefront");
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile (XOR swizzle by
+// row, as in the forward kernel).
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+}
+
+// fp32 value m as three bf16 parts (hi + mid + lo == m to fp32 precision) in slots 0..2 of
+// the lanes of channel group 0: with an operand of ones in the same slots, one MFMA step
+// adds -m (sign folded) to a whole row or column of an accumulator.
+__device__ __forceinline__ bf16x8 fold_neg(float m, int g) {
+  const float nm = -m;
+  const __bf16 hi = (__bf16)nm;
+  const float r1 = nm - (float)hi;
+  const __bf16 mid = (__bf16)r1;
+  const __bf16 lo = (__bf16)(r1 - (float)mid);
+  const __bf16 z = (__bf16)0.0f;
+  const bf16x8 v = {hi, mid, lo, z, z, z, z, z};
+  const bf16x8 zero = {z, z, z, z, z, z, z, z};
+  return g == 0 ? v : zero;
+}
+
+__device__ __forceinline__ bf16x8 ones_slots(int g) {
+  const __bf16 one = (__bf16)1.0f, z = (__bf16)0.0f;
+  return g == 0 ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
+}
+
+// 8 channels (chunk c) of row `row` of a [rows, 64] bf16 tensor as an MFMA operand; zero
+// when !ok.
+__device__ __forceinline__ bf16x8 load_chunk(const uint16_t* base, int64_t row, int c, bool ok) {
+  u32x4 raw{0u, 0u, 0u, 0u};
+  if (ok) raw = *reinterpret_cast<const u32x4*>(base + row * 64 + 8 * c);
+  return __builtin_bit_cast(bf16x8, raw);
+}
+
+// 16 accumulator values (scores of one 32 x 32 tile) -> bf16 MFMA B operands of its two
+// 16-wide contraction steps (registers 8h .. 8h+7 of step h).
+__device__ __forceinline__ void pack16(const f32x16& x, bf16x8 (&b)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    bf16x2 w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const f32x2_t p = {x[8 * h + 2 * e2], x[8 * h + 2 * e2 + 1]};
+      w[e2] = __builtin_convertvector(p, bf16x2);
+    }
+    b[h] = __builtin_shufflevector(__builtin_shufflevector(w[0], w[1], 0, 1, 2, 3),
+                                   __builtin_shufflevector(w[2], w[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// Offsets of the transposing reads that give the A operand X^T of a contraction over the
+// rows of a row-major tile X (the rows in the order in which an accumulator holds them):
+// channel tile dt, plus 2048 * (2 * half + step) for the 16 rows of a step.
+__device__ __forceinline__ uint32_t tr_off(int lane, int dt) {
+  const int g = lane >> 5;
+  const int row0 = 4 * g + ((lane & 15) >> 2);
+  const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return tile_off(row0, col >> 3) + (uint32_t)(lane & 1) * 8u;
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const unsigned char* tile, uint32_t off) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off + 1024u));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Asynchronous copy of rows 64*blk .. 64*blk+63 (clamped to the sequence) of a [N, 64] bf16
+// slice into an LDS tile: wavefront w moves rows 8w .. 8w+7, lane l row 8w + l/8, landing at
+// physical chunk l%8, which holds logical chunk (l%8) ^ (row%8) of the swizzle.
+__device__ __forceinline__ void copy_tile(const uint16_t* slice, int32_t N, int blk, unsigned char* dst, int wave,
+                                          int lane) {
+  const int row = 8 * wave + (lane >> 3);
+  int t = 64 * blk + row;
+  t = t < N ? t : N - 1;
+  const int gch = (lane & 7) ^ (lane >> 3);
+  __builtin_amdgcn_global_load_lds(slice + (int64_t)t * 64 + 8 * gch, (lds_void*)(dst + 1024 * wave), 16, 0, 0);
+}
+
+// Asynchronous copy of 64 fp32 row values (clamped) into LDS (one wavefront).
+__device__ __forceinline__ void copy_rows_f32(const float* slice, int32_t N, int blk, float* dst, int lane) {
+  int t = 64 * blk + lane;
+  t = t < N ? t : N - 1;
+  __builtin_amdgcn_global_load_lds(slice + t, (lds_void*)dst, 4, 0, 0);
+}
+
+// D = rowsum(dO * O) and 8 * lse per row; one thread per 8-channel chunk of a row.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* out, const uint16_t* dout, const float* lse,
+                                                       float* lse8, float* delta, int64_t rows) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 3;
+  const int c = (int)(gid & 7);
+  if (row >= rows) return;   // the eight lanes of a row leave together
+  const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * 64 + 8 * c);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * 64 + 8 * c);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), s);
+    s = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), s);
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  if (c == 0) {
+    delta[row] = s;
+    const float l = lse[row];
+    lse8[row] = (l == -INFINITY) ? kEmptyRowLse8 : 8.0f * l;
+  }
+}
+
+// Work item -> workgroup numbering as in the forward: XCD x (blockIdx % 8) runs the x-th
+// contiguous eighth of the items.
+__device__ __forceinline__ int xcd_item() {
+  const int per_xcd = (int)(gridDim.x >> 3);
+  return (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+}
+
+// ------------------------------------------------------------------------------------ dQ
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams P) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int item = xcd_item();
+  if (item >= P.bh * P.n_st) return;
+  const int bh = item / P.n_st;
+  const int st = item - bh * P.n_st;
+  const int64_t base = (int64_t)bh * P.N;
+
+  // this wavefront's 32 query rows; the lane's own row is q
+  const int qblk = st * kWaves + (wave >> 1);
+  const bool wave_on = qblk < P.n_blocks;
+  const int q = 64 * qblk + 32 * (wave & 1) + l32;
+  const bool qok = wave_on && q < P.N;
+  bf16x8 qf[4], dof[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qf[ks] = load_chunk(P.q + base * 64, q, 2 * ks + g, qok);
+    dof[ks] = load_chunk(P.dout + base * 64, q, 2 * ks + g, qok);
+  }
+  const float lse8 = qok ? P.lse8[base + q] : kEmptyRowLse8;
+  const float dlt = qok ? P.delta[base + q] : 0.f;
+  const bf16x8 fold_l = fold_neg(lse8, g);
+  const bf16x8 fold_d = fold_neg(dlt, g);
+  const bf16x8 ones = ones_slots(g);
+  uint32_t ka_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
+  const uint32_t tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
+
+  f32x16 dqt[2];   // dQ^T tiles [channel tile]: lane = query, registers = channels
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
+
+  const int32_t* ents = P.st_ent + P.row_ptr[st * kWaves];
+  const int cnt = P.st_cnt[st];
+  const uint16_t* kslice = P.k + base * 64;
+  const uint16_t* vslice = P.v + base * 64;
+  int ent_cur = 0, ent_next = 0;
+  if (cnt > 0) {
+    ent_cur = __builtin_amdgcn_readfirstlane(ents[0]);
+    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(ents[1]);
+    copy_tile(kslice, P.N, ent_cur >> 8, lds_k0, wave, lane);
+    copy_tile(vslice, P.N, ent_cur >> 8, lds_v0, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, bool masked) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 ka[4], va[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
+        va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
+      }
+      // S^T - 8 lse and dP^T - D for keys 32kt .. 32kt+31
+      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
+      f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dof[ks], dp, 0, 0, 0);
+      }
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * j + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = key < P.N && (q >= P.C || key < P.C);
+          s[r] = ok ? s[r] : -INFINITY;
+        }
+      }
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(s[r] * kScoreToLog2) * dp[r];
+      bf16x8 dsb[2];
+      pack16(ds, dsb);
+      // dQ^T += K^T dS^T over the two 16-key steps of the half
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t so = 2048u * (2 * kt + h);
+        dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0 + so), dsb[h], dqt[0], 0, 0, 0);
+        dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1 + so), dsb[h], dqt[1], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&](auto stage_tag, int e) __attribute__((always_inline)) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    unsigned char* const kc = STAGE ? lds_k1 : lds_k0;
+    unsigned char* const vc = STAGE ? lds_v1 : lds_v0;
+    unsigned char* const kn = STAGE ? lds_k0 : lds_k1;
+    unsigned char* const vn = STAGE ? lds_v0 : lds_v1;
+    const int ent = ent_cur;
+    // next block's copies (past the end of the list they re-read block 0 into a free stage)
+    copy_tile(kslice, P.N, ent_next >> 8, kn, wave, lane);
+    copy_tile(vslice, P.N, ent_next >> 8, vn, wave, lane);
+    const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
+    if (wave_on && ((ent >> (wave >> 1)) & 1)) {
+      const int j = ent >> 8;
+      const bool masked = 64 * j + 63 >= P.N || (64 * qblk < P.C && 64 * j + 63 >= P.C);
+      if (masked)
+        block(kc, vc, j, true);
+      else
+        block(kc, vc, j, false);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    ent_cur = ent_next;
+    ent_next = __builtin_amdgcn_readfirstlane(ent_after_raw);
+  };
+  int e = 0;
+  for (; e + 1 < cnt; e += 2) {
+    step(std::integral_constant<int, 0>{}, e);
+    step(std::integral_constant<int, 1>{}, e + 1);
+  }
+  if (e < cnt) step(std::integral_constant<int, 0>{}, e);
+
+  // dQ = dQ^T / 8 (the score scale), rows written as 8-byte stores of 4 channels
+  if (qok) {
+    uint16_t* row = P.dq + (base + q) * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        uint2 pk;
+        pk.x = pack_bf16x2(dqt[dt][4 * R] * 0.125f, dqt[dt][4 * R + 1] * 0.125f);
+        pk.y = pack_bf16x2(dqt[dt][4 * R + 2] * 0.125f, dqt[dt][4 * R + 3] * 0.125f);
+        *reinterpret_cast<uint2*>(row + 32 * dt + 8 * R + 4 * g) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------- dK, dV
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParams P) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_q0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_q1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_o0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_o1[kTileBytes];
+  __shared__ __attribute__((aligned(256))) float lds_l0[64];
+  __shared__ __attribute__((aligned(256))) float lds_l1[64];
+  __shared__ __attribute__((aligned(256))) float lds_d0[64];
+  __shared__ __attribute__((aligned(256))) float lds_d1[64];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int item = xcd_item();
+  if (item >= P.bh * P.n_kg) return;
+  const int bh = item / P.n_kg;
+  const int grp = item - bh * P.n_kg;
+  const int64_t base = (int64_t)bh * P.N;
+
+  // this wavefront's 32 keys; the lane's own key is key
+  const int kblk = __builtin_amdgcn_readfirstlane(P.kg_blk[grp * kWaves + (wave >> 1)]);
+  const bool wave_on = kblk >= 0;
+  const int key = 64 * kblk + 32 * (wave & 1) + l32;
+  const bool kok = wave_on && key < P.N;
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = load_chunk(P.k + base * 64, key, 2 * ks + g, kok);
+    vf[ks] = load_chunk(P.v + base * 64, key, 2 * ks + g, kok);
+  }
+  const bf16x8 ones = ones_slots(g);
+  uint32_t qa_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qa_off[ks] = tile_off(l32, 2 * ks + g);
+  const uint32_t tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
+
+  f32x16 dvt[2], dkt[2];   // dV^T, dK^T tiles [channel tile]: lane = key, registers = channels
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dvt[dt][r] = 0.f;
+      dkt[dt][r] = 0.f;
+    }
+
+  const int32_t* ents = P.kg_ent + P.kg_off[grp];
+  const int cnt = P.kg_cnt[grp];
+  const uint16_t* qslice = P.q + base * 64;
+  const uint16_t* oslice = P.dout + base * 64;
+  const float* lslice = P.lse8 + base;
+  const float* dslice = P.delta + base;
+  auto copies = [&](int blk, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
+    copy_tile(qslice, P.N, blk, qd, wave, lane);
+    copy_tile(oslice, P.N, blk, od, wave, lane);
+    if (wave == 0) copy_rows_f32(lslice, P.N, blk, ld, lane);
+    if (wave == 1) copy_rows_f32(dslice, P.N, blk, dd, lane);
+  };
+  int ent_cur = 0, ent_next = 0;
+  if (cnt > 0) {
+    ent_cur = __builtin_amdgcn_readfirstlane(ents[0]);
+    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(ents[1]);
+    copies(ent_cur >> 8, lds_q0, lds_o0, lds_l0, lds_d0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto block = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int i,
+                   bool masked) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      bf16x8 qa[4], oa[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qa[ks] = *reinterpret_cast<const bf16x8*>(qb + qa_off[ks] + 4096u * qt);
+        oa[ks] = *reinterpret_cast<const bf16x8*>(ob + qa_off[ks] + 4096u * qt);
+      }
+      // S - 8 lse and dP - D for queries 32qt .. 32qt+31 (rows) and this
+      // wavefront's keys (columns)
+      const bf16x8 fold_l = fold_neg(lb[32 * qt + l32], g);
+      const bf16x8 fold_d = fold_neg(db[32 * qt + l32], g);
+      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_l, ones, f32x16{}, 0, 0, 0);
+      f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_d, ones, f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks], vf[ks], dp, 0, 0, 0);
+      }
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = 64 * i + 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = qq < P.N && (qq >= P.C || key < P.C);
+          s[r] = ok ? s[r] : -INFINITY;
+        }
+      }
+      f32x16 p, ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(s[r] * kScoreToLog2);
+        ds[r] = p[r] * dp[r];
+      }
+      bf16x8 pb[2], dsb[2];
+      pack16(p, pb);
+      pack16(ds, dsb);
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query steps
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t so = 2048u * (2 * qt + h);
+        dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr0 + so), pb[h], dvt[0], 0, 0, 0);
+        dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr1 + so), pb[h], dvt[1], 0, 0, 0);
+        dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr0 + so), dsb[h], dkt[0], 0, 0, 0);
+        dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr1 + so), dsb[h], dkt[1], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&](auto stage_tag, int e) __attribute__((always_inline)) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    const unsigned char* const qc = STAGE ? lds_q1 : lds_q0;
+    const unsigned char* const oc = STAGE ? lds_o1 : lds_o0;
+    const float* const lc = STAGE ? lds_l1 : lds_l0;
+    const float* const dc = STAGE ? lds_d1 : lds_d0;
+    const int ent = ent_cur;
+    if (STAGE)
+      copies(ent_next >> 8, lds_q0, lds_o0, lds_l0, lds_d0);
+    else
+      copies(ent_next >> 8, lds_q1, lds_o1, lds_l1, lds_d1);
+    const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
+    if (wave_on && ((ent >> (wave >> 1)) & 1)) {
+      const int i = ent >> 8;
+      const bool masked = 64 * i + 63 >= P.N || (64 * i < P.C && 64 * kblk + 63 >= P.C);
+      if (masked)
+        block(qc, oc, lc, dc, i, true);
+      else
+        block(qc, oc, lc, dc, i, false);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    ent_cur = ent_next;
+    ent_next = __builtin_amdgcn_readfirstlane(ent_after_raw);
+  };
+  int e = 0;
+  for (; e + 1 < cnt; e += 2) {
+    step(std::integral_constant<int, 0>{}, e);
+    step(std::integral_constant<int, 1>{}, e + 1);
+  }
+  if (e < cnt) step(std::integral_constant<int, 0>{}, e);
+
+  // dK = dK^T / 8, dV = dV^T; key rows written as 8-byte stores of 4 channels
+  if (kok) {
+    uint16_t* krow = P.dk + (base + key) * 64;
+    uint16_t* vrow = P.dv + (base + key) * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        uint2 pk, pv;
+        pk.x = pack_bf16x2(dkt[dt][4 * R] * 0.125f, dkt[dt][4 * R + 1] * 0.125f);
+        pk.y = pack_bf16x2(dkt[dt][4 * R + 2] * 0.125f, dkt[dt][4 * R + 3] * 0.125f);
+        pv.x = pack_bf16x2(dvt[dt][4 * R], dvt[dt][4 * R + 1]);
+        pv.y = pack_bf16x2(dvt[dt][4 * R + 2], dvt[dt][4 * R + 3]);
+        *reinterpret_cast<uint2*>(krow + 32 * dt + 8 * R + 4 * g) = pk;
+        *reinterpret_cast<uint2*>(vrow + 32 * dt + 8 * R + 4 * g) = pv;
+      }
+  }
+}
+
+unsigned grid_for(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
+
+}  // namespace
+
+hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.bh_rows == 0) return hipSuccess;
+  const int64_t threads = p.bh_rows * 8;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.out, p.dout,
+                     p.lse, p.lse8, p.delta, p.bh_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid_for((int64_t)p.bh * p.n_kg)), dim3(kBwdThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace lcv

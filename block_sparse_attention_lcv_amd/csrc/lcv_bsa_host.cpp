@@ -6,6 +6,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "lcv_internal.h"
 
@@ -101,6 +102,54 @@ lcv_status compute_info(const lcv_bsa_layout_params* p, lcv_bsa_layout_info* inf
   info->nnz = nnz;
   info->attended_pairs = pairs;
   return LCV_OK;
+}
+
+// Key-side schedule of the backward (column walk), built on the host from the row rule:
+// the columns of the CSR, key blocks grouped kWaves at a time (the strided global blocks,
+// whose columns are nearly all rows, together; the others in ascending runs), and per group
+// the ascending union of its columns with a per-slot membership mask.
+struct KeyGroups {
+  std::vector<int32_t> blk, cnt, off, ent;
+};
+
+KeyGroups build_key_groups(const lcv::LayoutRule& L) {
+  std::vector<std::vector<int32_t>> col(L.n);
+  for (int32_t i = 0; i < L.n; ++i) {
+    const lcv::RowShape rs = lcv::row_shape(L, i);
+    for (int32_t r = 0; r < rs.len; ++r) col[lcv::row_elem(L, rs, r)].push_back(i);
+  }
+  std::vector<int32_t> order;
+  order.reserve(L.n);
+  for (int32_t j = 0; j < L.n; ++j)
+    if (L.s > 0 && j % L.s == 0) order.push_back(j);
+  for (int32_t j = 0; j < L.n; ++j)
+    if (!(L.s > 0 && j % L.s == 0)) order.push_back(j);
+  KeyGroups kg;
+  std::vector<int32_t> mask(L.n, 0);
+  for (size_t g0 = 0; g0 < order.size(); g0 += lcv::kWaves) {
+    int32_t lo = L.n, hi = -1;
+    for (int b = 0; b < lcv::kWaves; ++b) {
+      const size_t idx = g0 + b;
+      const int32_t j = idx < order.size() ? order[idx] : -1;
+      kg.blk.push_back(j);
+      if (j < 0) continue;
+      for (int32_t i : col[j]) {
+        mask[i] |= 1 << b;
+        lo = i < lo ? i : lo;
+        hi = i > hi ? i : hi;
+      }
+    }
+    kg.off.push_back((int32_t)kg.ent.size());
+    int32_t c = 0;
+    for (int32_t i = lo; i <= hi; ++i)
+      if (mask[i] != 0) {
+        kg.ent.push_back((i << 8) | mask[i]);
+        mask[i] = 0;
+        ++c;
+      }
+    kg.cnt.push_back(c);
+  }
+  return kg;
 }
 
 lcv_status check_grid(const lcv_rope3d_grid* grid) {
@@ -276,6 +325,25 @@ lcv_status lcv_bsa_build_layout(const lcv_bsa_layout_params* params, hipStream_t
     lcv_bsa_layout_destroy(h);
     return fail(LCV_ERR_HIP, "layout build produced %d entries, expected %lld", gpu_nnz, (long long)info.nnz);
   }
+  // key-side schedule of the backward
+  const KeyGroups kg = build_key_groups(L);
+  h->dev.n_kg = (int32_t)kg.cnt.size();
+  h->dev.kg_total = (int64_t)kg.ent.size();
+  struct {
+    int32_t** p;
+    const std::vector<int32_t>* v;
+  } kbufs[] = {{&h->dev.kg_blk, &kg.blk}, {&h->dev.kg_cnt, &kg.cnt}, {&h->dev.kg_off, &kg.off},
+               {&h->dev.kg_ent, &kg.ent}};
+  for (auto& b : kbufs) {
+    const size_t bytes = (b.v->empty() ? 1 : b.v->size()) * sizeof(int32_t);
+    e = hipMalloc(reinterpret_cast<void**>(b.p), bytes);
+    if (e == hipSuccess && !b.v->empty())
+      e = hipMemcpy(*b.p, b.v->data(), b.v->size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      lcv_bsa_layout_destroy(h);
+      return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "backward schedule: %s", hipGetErrorString(e));
+    }
+  }
   *out = h;
   return ok();
 }
@@ -306,6 +374,10 @@ void lcv_bsa_layout_destroy(lcv_bsa_layout* layout) {
   (void)hipFree(layout->dev.col_idx);
   (void)hipFree(layout->dev.st_cnt);
   (void)hipFree(layout->dev.st_ent);
+  (void)hipFree(layout->dev.kg_blk);
+  (void)hipFree(layout->dev.kg_cnt);
+  (void)hipFree(layout->dev.kg_off);
+  (void)hipFree(layout->dev.kg_ent);
   delete layout;
 }
 
@@ -352,6 +424,61 @@ lcv_status lcv_qk_rmsnorm_rope3d(const void* x, void* y, const float* gamma, flo
       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), gamma, eps, n_outer, n_tokens, token_offset,
       grid != nullptr, grid ? grid->H : 1, grid ? grid->W : 1, grid ? std::log2(grid->theta) : 0.f, stream);
   if (e != hipSuccess) return hip_fail(e, "qk prologue launch");
+  return ok();
+}
+
+lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
+                            int32_t cond_len, void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr || layout == nullptr)
+    return fail(LCV_ERR_NULL, "every tensor, the workspace and the layout are required");
+  if (batch < 1 || heads < 1) return fail(LCV_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if (cond_len != layout->info.cond_len)
+    return fail(LCV_ERR_LAYOUT_MISMATCH, "cond_len %d differs from the layout's %d", cond_len, layout->info.cond_len);
+  for (const void* t : {q, k, v, out, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (!aligned(t, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(workspace, 4)) return fail(LCV_ERR_INVALID_ARG, "lse and workspace must be 4-byte aligned");
+  const int64_t bh = (int64_t)batch * heads;
+  const int32_t N = layout->info.n_tokens;
+  const int64_t items = bh * (layout->dev.n_st > layout->dev.n_kg ? layout->dev.n_st : layout->dev.n_kg);
+  if (bh >= (int64_t(1) << 31) || items >= (int64_t(1) << 31) - 8 || bh * N * 8 >= (int64_t(1) << 40))
+    return fail(LCV_ERR_UNSUPPORTED, "batch * heads = %lld is too large", (long long)bh);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != layout->device)
+    return fail(LCV_ERR_INVALID_ARG, "layout was built on device %d, current device is %d", layout->device, dev);
+  lcv::BwdParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.lse8 = workspace;
+  p.delta = workspace + bh * N;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.row_ptr = layout->dev.row_ptr;
+  p.st_cnt = layout->dev.st_cnt;
+  p.st_ent = layout->dev.st_ent;
+  p.kg_blk = layout->dev.kg_blk;
+  p.kg_cnt = layout->dev.kg_cnt;
+  p.kg_off = layout->dev.kg_off;
+  p.kg_ent = layout->dev.kg_ent;
+  p.bh_rows = bh * N;
+  p.N = N;
+  p.C = cond_len;
+  p.n_blocks = layout->info.n_blocks;
+  p.n_st = layout->dev.n_st;
+  p.n_kg = layout->dev.n_kg;
+  p.bh = (int32_t)bh;
+  e = lcv::launch_bsa_bwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }
 

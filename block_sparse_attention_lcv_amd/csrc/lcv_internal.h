@@ -120,6 +120,16 @@ struct LayoutDev {
   int32_t* st_cnt;    // [n_st] entries of each workgroup's key-block list
   int32_t* st_ent;    // [nnz]   list of workgroup st starts at row_ptr[st*kWaves]: (j << 8) | wave mask
   int32_t n_st;       // ceil(n / kWaves)
+  // Key-side schedule of the backward (column walk): key blocks in groups of kWaves whose
+  // columns (attending query blocks) are nearly the same -- the strided global blocks
+  // together, the others in runs of consecutive blocks -- and per group the ascending union
+  // of its columns, entry (i << 8) | mask (bit b: query block i attends key block kg_blk[4g+b]).
+  int32_t* kg_blk;    // [n_kg * kWaves] key block of each slot, -1 for an empty slot
+  int32_t* kg_cnt;    // [n_kg]
+  int32_t* kg_off;    // [n_kg] first entry of each group's list in kg_ent
+  int32_t* kg_ent;    // [kg_total]
+  int32_t n_kg;
+  int64_t kg_total;
 };
 
 struct FwdParams {
@@ -147,7 +157,31 @@ struct FwdParams {
   int32_t rope_entries;     // 8T + 12H + 12W when a RoPE flag is set
 };
 
+struct BwdParams {
+  const uint16_t* q;        // [BH, N, 64], as it entered the scores (rotated)
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;      // forward output
+  const uint16_t* dout;     // upstream gradient
+  const float* lse;         // [BH, N] natural-log LSE of the forward
+  float* lse8;              // [BH, N] workspace: 8 * lse (3e38 for an empty row)
+  float* delta;             // [BH, N] workspace: rowsum(dout * out)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* row_ptr;
+  const int32_t* st_cnt;
+  const int32_t* st_ent;
+  const int32_t* kg_blk;
+  const int32_t* kg_cnt;
+  const int32_t* kg_off;
+  const int32_t* kg_ent;
+  int64_t bh_rows;          // BH * N
+  int32_t N, C, n_blocks, n_st, n_kg, bh;
+};
+
 hipError_t launch_layout_build(const LayoutRule& L, const LayoutDev& d, hipStream_t stream);
+hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int64_t n_outer, int32_t n_tokens,
                          int32_t token_offset, int32_t H, int32_t W, float log2_theta, hipStream_t stream);
 hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream);

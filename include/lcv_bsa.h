@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 2
+#define LCV_BSA_ABI_VERSION 3
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -180,6 +180,25 @@ lcv_status lcv_bsa_forward_cached(const void* q_noise, const void* k_noise, cons
                                   const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
                                   const lcv_rope3d_grid* grid, void* out_noise, float* lse_noise,
                                   hipStream_t stream);
+
+/* Backward of lcv_bsa_forward (flags = 0): the gradients of the attention for the upstream
+ * gradient dout, for training (myzaker article, technical principles: the LoRA-trained
+ * refinement expert; SimpleTuner quickstart "LongCat-Video Edit").  With P recomputed from
+ * the saved LSE: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)), dQ = dS K / 8,
+ * dK = dS^T Q / 8, under the same layout and condition rule as the forward.
+ *   q, k, v, out, dout : bf16 [batch, heads, N, 64]; q and k as they entered the scores (a
+ *                        caller that rotates with RoPE passes the rotated tensors and
+ *                        rotates dq, dk back), out the forward's output
+ *   lse                : fp32 [batch, heads, N], the forward's
+ *   dq, dk, dv         : bf16 [batch, heads, N, 64], written completely (fp32 accumulation)
+ *   workspace          : fp32 [2 * batch * heads * N] scratch, caller-owned (8 B per row)
+ * Deterministic: every output row is written once, without atomics.  Asynchronous on
+ * stream.  Errors: NULL, INVALID_ARG (sizes, alignment, device), LAYOUT_MISMATCH (cond_len),
+ * UNSUPPORTED (sizes), HIP. */
+lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
+                            int32_t cond_len, void* dq, void* dk, void* dv, float* workspace,
+                            hipStream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* lcv_last_error(void);

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 2
+    assert bsa.lib().lcv_abi_version() == 3
 
 
 QUERY_CASES = [
@@ -100,6 +100,17 @@ def test_forward_requires_layout():
     assert L.lcv_bsa_layout_get_info(None, None) == 1
     assert L.lcv_bsa_layout_copy_csr(None, p, p, None) == 1
     L.lcv_bsa_layout_destroy(None)   # no-op
+
+
+def test_backward_argument_errors():
+    L = bsa.lib()
+    p = ctypes.c_void_p(4096)
+    f = L.lcv_bsa_backward
+    assert f(p, p, p, p, p, p, 1, 1, None, 0, p, p, p, p, None) == 1          # no layout
+    assert f(p, p, p, p, p, p, 1, 1, None, 0, p, p, p, None, None) == 1       # no workspace
+    assert f(p, p, p, p, None, p, 1, 1, None, 0, p, p, p, p, None) == 1       # no lse
+    assert f(p, p, p, p, p, None, 1, 1, None, 0, p, p, p, p, None) == 1       # no dout
+    assert b"required" in L.lcv_last_error()
 
 
 def test_rope_argument_errors():
