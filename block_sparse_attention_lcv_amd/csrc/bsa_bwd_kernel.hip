@@ -35,19 +35,26 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+// read-only schedule tables through the constant address space: uniform indexes become scalar
+// loads, which neither occupy the vector memory counter nor need a readfirstlane
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 constexpr int kBwdWaves = 2 * kWaves;         // two wavefronts (32 rows each) per 64-row block
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kTileBytes = 64 * 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kScoreToLog2 = kLog2e / 8.0f;
-constexpr float kEmptyRowLse8 = 3.0e38f;      // 8 * lse of a row with no key: p = 0
+constexpr float kEmptyRowLse8 = 3.0e38f;
+// s_waitcnt operand: vmcnt <= 2 and lgkmcnt == 0, expcnt not waited for (gfx9 field layout)
+constexpr int kWaitVm2 = 2 | (7 << 4);      // 8 * lse of a row with no key: p = 0
 static_assert(kBwdWaves == 8, "a 64 x 64 tile is 8 wave-loads of 1 KB, one per wavefront");
 
-// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile (XOR swizzle by
-// row, as in the forward kernel).
+// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile (the forward
+// kernel's swizzle: row reads of one chunk and the transposing reads are free of bank
+// conflicts).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
 }
 
 // fp32 value m as three bf16 parts (hi + mid + lo == m to fp32 precision) in slots 0..2 of
@@ -112,13 +119,13 @@ __device__ __forceinline__ bf16x8 tr_read(const unsigned char* tile, uint32_t of
 
 // Asynchronous copy of rows 64*blk .. 64*blk+63 (clamped to the sequence) of a [N, 64] bf16
 // slice into an LDS tile: wavefront w moves rows 8w .. 8w+7, lane l row 8w + l/8, landing at
-// physical chunk l%8, which holds logical chunk (l%8) ^ (row%8) of the swizzle.
+// physical chunk l%8, which holds logical chunk (l%8) ^ swz(row%8) of the swizzle.
 __device__ __forceinline__ void copy_tile(const uint16_t* slice, int32_t N, int blk, unsigned char* dst, int wave,
                                           int lane) {
   const int row = 8 * wave + (lane >> 3);
   int t = 64 * blk + row;
   t = t < N ? t : N - 1;
-  const int gch = (lane & 7) ^ (lane >> 3);
+  const int gch = (lane & 7) ^ swz(lane >> 3);
   __builtin_amdgcn_global_load_lds(slice + (int64_t)t * 64 + 8 * gch, (lds_void*)(dst + 1024 * wave), 16, 0, 0);
 }
 
@@ -154,6 +161,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* out, cons
   }
 }
 
+// End of a pipeline step: this wavefront's copies of the next block have landed in LDS (only
+// the two copies issued in this step may still be in flight) and its LDS reads are done;
+// then the workgroup barrier.  __syncthreads() would also wait for the copies in flight
+// (its release fence covers every outstanding memory operation).
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitVm2);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Work item -> workgroup numbering as in the forward: XCD x (blockIdx % 8) runs the x-th
 // contiguous eighth of the items.
 __device__ __forceinline__ int xcd_item() {
@@ -167,6 +185,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v2[kTileBytes];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,9 +210,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
     qf[ks] = load_chunk(P.q + base * 64, q, 2 * ks + g, qok);
     dof[ks] = load_chunk(P.dout + base * 64, q, 2 * ks + g, qok);
   }
-  const float lse8 = qok ? P.lse8[base + q] : kEmptyRowLse8;
+  // the row's lse (log2 units) enters each exponent through one FMA (it is the lane's own
+  // constant); D is folded into the dP^T accumulator by one extra MFMA step
+  const float lse2 = (qok ? P.lse8[base + q] : kEmptyRowLse8) * kScoreToLog2;
   const float dlt = qok ? P.delta[base + q] : 0.f;
-  const bf16x8 fold_l = fold_neg(lse8, g);
   const bf16x8 fold_d = fold_neg(dlt, g);
   const bf16x8 ones = ones_slots(g);
   uint32_t ka_off[4];
@@ -206,90 +227,141 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
 
-  const int32_t* ents = P.st_ent + P.row_ptr[st * kWaves];
+  const const_i32* ents = (const const_i32*)(P.st_ent) + P.row_ptr[st * kWaves];
   const int cnt = P.st_cnt[st];
   const uint16_t* kslice = P.k + base * 64;
   const uint16_t* vslice = P.v + base * 64;
-  int ent_cur = 0, ent_next = 0;
+  // three LDS stages: block e+2 is copied while block e is used and block e+1 lands
+  int ent_cur = 0, ent_n1 = 0, ent_n2 = 0;
   if (cnt > 0) {
-    ent_cur = __builtin_amdgcn_readfirstlane(ents[0]);
-    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(ents[1]);
+    ent_cur = ents[0];
+    if (cnt > 1) ent_n1 = ents[1];
+    if (cnt > 2) ent_n2 = ents[2];
     copy_tile(kslice, P.N, ent_cur >> 8, lds_k0, wave, lane);
     copy_tile(vslice, P.N, ent_cur >> 8, lds_v0, wave, lane);
+    copy_tile(kslice, P.N, ent_n1 >> 8, lds_k1, wave, lane);
+    copy_tile(vslice, P.N, ent_n1 >> 8, lds_v1, wave, lane);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  stage_barrier();
 
-  auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, bool masked) __attribute__((always_inline)) {
+  // S^T and dP^T - D of keys 32kt .. 32kt+31 (registers) against the wavefront's queries
+  auto sdp_half = [&](const unsigned char* kb, const unsigned char* vb, int kt, f32x16& s, f32x16& dp)
+      __attribute__((always_inline)) {
+    bf16x8 ka[4], va[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      bf16x8 ka[4], va[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
-        va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
-      }
-      // S^T - 8 lse and dP^T - D for keys 32kt .. 32kt+31
-      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
-      f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dof[ks], dp, 0, 0, 0);
-      }
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * j + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < P.N && (q >= P.C || key < P.C);
-          s[r] = ok ? s[r] : -INFINITY;
-        }
-      }
-      f32x16 ds;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(s[r] * kScoreToLog2) * dp[r];
-      bf16x8 dsb[2];
-      pack16(ds, dsb);
-      // dQ^T += K^T dS^T over the two 16-key steps of the half
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t so = 2048u * (2 * kt + h);
-        dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0 + so), dsb[h], dqt[0], 0, 0, 0);
-        dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1 + so), dsb[h], dqt[1], 0, 0, 0);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
+      va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
     }
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks > 0) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dof[ks], dp, 0, 0, 0);
+    }
+  };
+  auto mask_half = [&](int j, int kt, f32x16& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 64 * j + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool ok = key < P.N && (q >= P.C || key < P.C);
+      s[r] = ok ? s[r] : -INFINITY;
+    }
+  };
+  // dS^T = P^T * (dP^T - D) as the bf16 B operands of the two 16-key steps
+  auto ds_half = [&](const f32x16& s, const f32x16& dp, bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(fmaf(s[r], kScoreToLog2, -lse2)) * dp[r];
+    pack16(ds, dsb);
+  };
+  // dQ^T += K^T dS^T over the two 16-key steps of half kt
+  auto dq_half = [&](const unsigned char* kb, int kt, const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t so = 2048u * (2 * kt + h);
+      dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0 + so), dsb[h], dqt[0], 0, 0, 0);
+      dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1 + so), dsb[h], dqt[1], 0, 0, 0);
+    }
+  };
+
+  // One key block, its halves software-pipelined as in the forward: the second half's S^T
+  // and dP^T go to the matrix cores while the vector ALU forms the first half's dS^T, and
+  // the first half's dQ^T update runs with the second half's dS^T.
+  auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, auto mask_tag, auto&& copies)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 d0[2], d1[2];
+    sdp_half(kb, vb, 0, s0, dp0);
+    if (MASK) mask_half(j, 0, s0);
+    copies();
+    sdp_half(kb, vb, 1, s1, dp1);
+    ds_half(s0, dp0, d0);
+    // 8 K/V reads, then the second half's 9 MFMAs each followed by vector work of the first
+    // half's dS^T
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    if (MASK) mask_half(j, 1, s1);
+    dq_half(kb, 0, d0);
+    ds_half(s1, dp1, d1);
+    // 8 transposing K reads, then the first half's 4 dQ^T MFMAs each followed by vector work
+    // of the second half's dS^T
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
+    dq_half(kb, 1, d1);
   };
 
   auto step = [&](auto stage_tag, int e) __attribute__((always_inline)) {
     constexpr int STAGE = decltype(stage_tag)::value;
-    unsigned char* const kc = STAGE ? lds_k1 : lds_k0;
-    unsigned char* const vc = STAGE ? lds_v1 : lds_v0;
-    unsigned char* const kn = STAGE ? lds_k0 : lds_k1;
-    unsigned char* const vn = STAGE ? lds_v0 : lds_v1;
+    constexpr int SN = (STAGE + 2) % 3;
+    unsigned char* const kc = STAGE == 0 ? lds_k0 : STAGE == 1 ? lds_k1 : lds_k2;
+    unsigned char* const vc = STAGE == 0 ? lds_v0 : STAGE == 1 ? lds_v1 : lds_v2;
+    unsigned char* const kn = SN == 0 ? lds_k0 : SN == 1 ? lds_k1 : lds_k2;
+    unsigned char* const vn = SN == 0 ? lds_v0 : SN == 1 ? lds_v1 : lds_v2;
     const int ent = ent_cur;
-    // next block's copies (past the end of the list they re-read block 0 into a free stage)
-    copy_tile(kslice, P.N, ent_next >> 8, kn, wave, lane);
-    copy_tile(vslice, P.N, ent_next >> 8, vn, wave, lane);
-    const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
+    const int jn = ent_n2 >> 8;
+    const int ent_after_raw = (e + 3 < cnt) ? ents[e + 3] : 0;
+    // copies of block e+2 into the stage block e-1 used (past the end of the list they
+    // re-read block 0, which nothing reads any more)
+    auto copies = [&]() __attribute__((always_inline)) {
+      copy_tile(kslice, P.N, jn, kn, wave, lane);
+      copy_tile(vslice, P.N, jn, vn, wave, lane);
+    };
     if (wave_on && ((ent >> (wave >> 1)) & 1)) {
       const int j = ent >> 8;
       const bool masked = 64 * j + 63 >= P.N || (64 * qblk < P.C && 64 * j + 63 >= P.C);
       if (masked)
-        block(kc, vc, j, true);
+        block(kc, vc, j, std::true_type{}, copies);
       else
-        block(kc, vc, j, false);
+        block(kc, vc, j, std::false_type{}, copies);
+    } else {
+      copies();
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    ent_cur = ent_next;
-    ent_next = __builtin_amdgcn_readfirstlane(ent_after_raw);
+    stage_barrier();
+    ent_cur = ent_n1;
+    ent_n1 = ent_n2;
+    ent_n2 = ent_after_raw;
   };
   int e = 0;
-  for (; e + 1 < cnt; e += 2) {
+  for (; e + 2 < cnt; e += 3) {
     step(std::integral_constant<int, 0>{}, e);
     step(std::integral_constant<int, 1>{}, e + 1);
+    step(std::integral_constant<int, 2>{}, e + 2);
   }
   if (e < cnt) step(std::integral_constant<int, 0>{}, e);
+  if (e + 1 < cnt) step(std::integral_constant<int, 1>{}, e + 1);
+  // the last copies (re-reads into free stages) land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
 
   // dQ = dQ^T / 8 (the score scale), rows written as 8-byte stores of 4 channels
   if (qok) {
@@ -375,54 +447,88 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto block = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int i,
-                   bool masked) __attribute__((always_inline)) {
+  // S - 8 lse and dP - D for queries 32qt .. 32qt+31 (registers) and the wavefront's keys
+  // (lanes); the per-query lse and D enter through one folded MFMA step each
+  auto sdp_half = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int qt,
+                      f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    bf16x8 qa[4], oa[4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      bf16x8 qa[4], oa[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        qa[ks] = *reinterpret_cast<const bf16x8*>(qb + qa_off[ks] + 4096u * qt);
-        oa[ks] = *reinterpret_cast<const bf16x8*>(ob + qa_off[ks] + 4096u * qt);
-      }
-      // S - 8 lse and dP - D for queries 32qt .. 32qt+31 (rows) and this
-      // wavefront's keys (columns)
-      const bf16x8 fold_l = fold_neg(lb[32 * qt + l32], g);
-      const bf16x8 fold_d = fold_neg(db[32 * qt + l32], g);
-      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_l, ones, f32x16{}, 0, 0, 0);
-      f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_d, ones, f32x16{}, 0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks], vf[ks], dp, 0, 0, 0);
-      }
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qq = 64 * i + 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = qq < P.N && (qq >= P.C || key < P.C);
-          s[r] = ok ? s[r] : -INFINITY;
-        }
-      }
-      f32x16 p, ds;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(s[r] * kScoreToLog2);
-        ds[r] = p[r] * dp[r];
-      }
-      bf16x8 pb[2], dsb[2];
-      pack16(p, pb);
-      pack16(ds, dsb);
-      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query steps
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t so = 2048u * (2 * qt + h);
-        dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr0 + so), pb[h], dvt[0], 0, 0, 0);
-        dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr1 + so), pb[h], dvt[1], 0, 0, 0);
-        dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr0 + so), dsb[h], dkt[0], 0, 0, 0);
-        dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr1 + so), dsb[h], dkt[1], 0, 0, 0);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      qa[ks] = *reinterpret_cast<const bf16x8*>(qb + qa_off[ks] + 4096u * qt);
+      oa[ks] = *reinterpret_cast<const bf16x8*>(ob + qa_off[ks] + 4096u * qt);
     }
+    const bf16x8 fold_l = fold_neg(lb[32 * qt + l32], g);
+    const bf16x8 fold_d = fold_neg(db[32 * qt + l32], g);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_l, ones, f32x16{}, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_d, ones, f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks], vf[ks], dp, 0, 0, 0);
+    }
+  };
+  auto mask_half = [&](int i, int qt, f32x16& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = 64 * i + 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool ok = qq < P.N && (qq >= P.C || key < P.C);
+      s[r] = ok ? s[r] : -INFINITY;
+    }
+  };
+  // P and dS = P * (dP - D) as the bf16 B operands of the two 16-query steps
+  auto pds_half = [&](const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2])
+      __attribute__((always_inline)) {
+    f32x16 p, ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(s[r] * kScoreToLog2);
+      ds[r] = p[r] * dp[r];
+    }
+    pack16(p, pb);
+    pack16(ds, dsb);
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query steps of half qt
+  auto upd_half = [&](const unsigned char* qb, const unsigned char* ob, int qt, const bf16x8 (&pb)[2],
+                      const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t so = 2048u * (2 * qt + h);
+      dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr0 + so), pb[h], dvt[0], 0, 0, 0);
+      dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr1 + so), pb[h], dvt[1], 0, 0, 0);
+      dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr0 + so), dsb[h], dkt[0], 0, 0, 0);
+      dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr1 + so), dsb[h], dkt[1], 0, 0, 0);
+    }
+  };
+
+  // One query block, its halves software-pipelined: the second half's S and dP go to the
+  // matrix cores while the vector ALU forms the first half's P and dS, and the first half's
+  // dV^T, dK^T updates run with the second half's P and dS.
+  auto block = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int i,
+                   auto mask_tag, auto&& copies) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 p0[2], d0[2], p1[2], d1[2];
+    sdp_half(qb, ob, lb, db, 0, s0, dp0);
+    if (MASK) mask_half(i, 0, s0);
+    copies();
+    sdp_half(qb, ob, lb, db, 1, s1, dp1);
+    pds_half(s0, dp0, p0, d0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+    for (int n = 0; n < 10; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    if (MASK) mask_half(i, 1, s1);
+    upd_half(qb, ob, 0, p0, d0);
+    pds_half(s1, dp1, p1, d1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    upd_half(qb, ob, 1, p1, d1);
   };
 
   auto step = [&](auto stage_tag, int e) __attribute__((always_inline)) {
@@ -432,18 +538,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     const float* const lc = STAGE ? lds_l1 : lds_l0;
     const float* const dc = STAGE ? lds_d1 : lds_d0;
     const int ent = ent_cur;
-    if (STAGE)
-      copies(ent_next >> 8, lds_q0, lds_o0, lds_l0, lds_d0);
-    else
-      copies(ent_next >> 8, lds_q1, lds_o1, lds_l1, lds_d1);
+    const int in = ent_next >> 8;
+    auto next_copies = [&]() __attribute__((always_inline)) {
+      if (STAGE)
+        copies(in, lds_q0, lds_o0, lds_l0, lds_d0);
+      else
+        copies(in, lds_q1, lds_o1, lds_l1, lds_d1);
+    };
     const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
     if (wave_on && ((ent >> (wave >> 1)) & 1)) {
       const int i = ent >> 8;
       const bool masked = 64 * i + 63 >= P.N || (64 * i < P.C && 64 * kblk + 63 >= P.C);
       if (masked)
-        block(qc, oc, lc, dc, i, true);
+        block(qc, oc, lc, dc, i, std::true_type{}, next_copies);
       else
-        block(qc, oc, lc, dc, i, false);
+        block(qc, oc, lc, dc, i, std::false_type{}, next_copies);
+    } else {
+      next_copies();
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

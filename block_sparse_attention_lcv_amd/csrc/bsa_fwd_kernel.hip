@@ -61,9 +61,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile; chunks are
-// XOR-swizzled by the row so that column reads of 8 consecutive rows hit distinct banks.
+// XOR-swizzled by swz(row), a permutation of 0..7 over each 8 rows, so that the 16-byte
+// reads of one chunk in 8 consecutive rows hit distinct banks, and so that the transposing
+// 8-byte reads (a chunk pair of 4 consecutive rows per 16 lanes) do too: swz(row) / 2 takes
+// 4 distinct values on every aligned group of 4 rows.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
 }
 
 __device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
@@ -97,7 +101,7 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 raw, int c, const Coords& xyz,
 // Staging of K/V block j into an LDS stage.  The 8 KB tile is moved as 8 wave-loads of
 // 1 KB (8 rows); wavefront w issues loads u = w*kLoadsPerWave + c.  In load u, lane l carries
 // row 8u + l/8 and lands at LDS byte 1024u + 16l, i.e. physical chunk l%8 of that row, which
-// holds logical chunk (l%8) ^ (row%8) under the XOR swizzle of tile_off.  Rows past the end
+// holds logical chunk (l%8) ^ swz(row%8) under the swizzle of tile_off.  Rows past the end
 // of the sequence read row N-1 (finite data; their scores are masked and their
 // probabilities are zero).
 constexpr int kLoadsPerWave = 8 / kWaves;
@@ -118,7 +122,7 @@ __device__ __forceinline__ const uint16_t* kv_row(const FwdParams& P, const uint
 template <bool ROPE_K, bool CACHED>
 __device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* kdst, unsigned char* vdst, int bh, int j,
                                             int wave, int lane, u32x4 (&kreg)[kLoadsPerWave]) {
-  const int gch = (lane & 7) ^ (lane >> 3);
+  const int gch = (lane & 7) ^ swz(lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
@@ -136,7 +140,7 @@ __device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* k
 // Rotate the K chunks loaded into kreg and write them to the stage (fused K RoPE only).
 __device__ __forceinline__ void stage_store_k(const FwdParams& P, unsigned char* stage, int j, int wave, int lane,
                                               const float2* tab, const u32x4 (&kreg)[kLoadsPerWave]) {
-  const int gch = (lane & 7) ^ (lane >> 3);
+  const int gch = (lane & 7) ^ swz(lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
