@@ -115,6 +115,21 @@ def grad_bits(seed: int, batch: int, heads: int, n_tokens: int) -> np.ndarray:
     return normal_bf16(rng, (batch, heads, n_tokens, HEAD_DIM))
 
 
+# Text states for the cross-attention: the pages name the text encoder (Qwen-2.5-VL) but no
+# prompt length; 512 tokens per prompt is taken as the padded length.
+TEXT_LEN = 512
+
+
+def text_kv_bits(seed: int, batch: int, heads: int, text_len: int = TEXT_LEN):
+    """Text keys and values of the cross-attention as bf16 bit patterns [batch, heads,
+    text_len, 64]: i.i.d. N(0,1) from their own PCG64 stream (seed + 20000), k then v."""
+    rng = np.random.Generator(np.random.PCG64(seed + 20000))
+    shape = (batch, heads, text_len, HEAD_DIM)
+    k = normal_bf16(rng, shape)
+    v = normal_bf16(rng, shape)
+    return k, v
+
+
 def workload_inputs(w: Workload, call: int = 0, q_scale: float = 1.0):
     """Inputs of a workload.  call 0: full Q/K/V over all N tokens.  call 1 (cached
     workloads): fresh noise-token Q/K/V over the N-C noise tokens, seed + 100."""

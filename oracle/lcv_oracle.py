@@ -28,6 +28,10 @@ fusion or reordering beyond what that definition states:
 * the query/key prologue: RMSNorm over each head's 64 channels with a per-channel gain,
   then the 3D-RoPE  [myzaker article, section on technical principles: RMSNorm in the
   self-attention module, 3D RoPE on visual tokens];
+* cross-attention of the video tokens' queries over the text states' keys and values (the
+  second attention of every DiT block  [myzaker article, technical principles: each block is
+  3D self-attention, cross-attention and a SwiGLU feed-forward network]): dense softmax
+  attention over the first kv_len[b] text tokens of each batch item (the rest is padding);
 * the gradients of the attention with respect to q, k, v (the backward pass that LoRA
   training of the model needs  [myzaker article, technical principles: the LoRA-trained
   refinement expert; SimpleTuner quickstart "LongCat-Video Edit", LoRA training]) by the
@@ -39,7 +43,8 @@ a radius; global blocks are key columns j % s == 0 (s == 0 disables them); block
 C tokens; noise rows attend by the layout alone; RoPE pairs are adjacent channels,
 integer positions from 0, theta = 1e4; attention is bidirectional; a row with no
 attended key yields out = 0 and lse = -inf; RMSNorm works per head over its 64 channels
-with one 64-value gain and is applied before the rotation.
+with one 64-value gain and is applied before the rotation; cross-attention has no RoPE and
+no block sparsity, and text tokens past a batch item's length are padding.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to properties fixed
 by the pages or by mathematics; nothing here is unpinned.
@@ -296,6 +301,28 @@ def bsa_forward(q, k, v, grid, cond_len: int, local: int, stride: int, theta: fl
             if rope_k:
                 kb = rope3d(kb, grid, theta)
             out[b, h], lse[b, h] = masked_attention(qb, kb, v[b, h], mask)
+    return out, lse
+
+
+def cross_attention(q, k, v, kv_lens=None, rows=None):
+    """Cross-attention of the video queries q [B, H, N, 64] over text keys/values
+    k, v [B, H, L, 64] (float64): softmax(q k^T / 8) v over the keys k < kv_lens[b] of each
+    batch item (all L when kv_lens is None).  rows: optional query indices (all if None).
+    Returns out [B, H, R, 64] and lse [B, H, R]; a batch item with no key gives out = 0 and
+    lse = -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    bsz, heads, n_q, _ = q.shape
+    n_kv = k.shape[2]
+    rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((bsz, heads, rows.size, HEAD_DIM))
+    lse = np.zeros((bsz, heads, rows.size))
+    for b in range(bsz):
+        length = n_kv if kv_lens is None else int(kv_lens[b])
+        mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (rows.size, n_kv))
+        for h in range(heads):
+            out[b, h], lse[b, h] = masked_attention(q[b, h, rows], k[b, h], v[b, h], mask)
     return out, lse
 
 

@@ -505,6 +505,65 @@ def pin_backward_sampled_match_full(impl):
     assert np.array_equal(impl.token_mask(rows, keys, cond, local, stride), allowed[np.ix_(rows, keys)])
 
 
+# ------------------------------------------------------------------------- cross-attention
+def pin_cross_dense_sdpa(impl):
+    """Without padding, cross-attention is plain softmax attention of the video queries over
+    the text keys: torch's scaled_dot_product_attention and logsumexp in float64."""
+    import torch
+    rng = np.random.default_rng(61)
+    q = rng.standard_normal((2, 3, 150, 64))
+    k = rng.standard_normal((2, 3, 77, 64))
+    v = rng.standard_normal((2, 3, 77, 64))
+    out, lse = impl.cross_attention(q, k, v)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+    ref_lse = torch.logsumexp(tq @ tk.transpose(-1, -2) / 8.0, dim=-1).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+    assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
+def pin_cross_padding(impl):
+    """Padding: with kv_lens, batch item b equals the unpadded attention over its first
+    kv_lens[b] text tokens, whatever the padded keys and values hold (bitwise); a length of
+    zero gives out = 0, lse = -inf; sampled rows equal the full result (to rounding)."""
+    rng = np.random.default_rng(62)
+    q = rng.standard_normal((3, 2, 90, 64))
+    k = rng.standard_normal((3, 2, 40, 64))
+    v = rng.standard_normal((3, 2, 40, 64))
+    lens = [40, 13, 0]
+    out, lse = impl.cross_attention(q, k, v, kv_lens=lens)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, 13:] = 1e3
+    v2[1, :, 13:] = -7.0
+    out2, lse2 = impl.cross_attention(q, k2, v2, kv_lens=lens)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    o1, l1 = impl.cross_attention(q[1:2], k[1:2, :, :13], v[1:2, :, :13])
+    assert np.max(np.abs(out[1:2] - o1)) < 1e-12 and np.max(np.abs(lse[1:2] - l1)) < 1e-12
+    o0, l0 = impl.cross_attention(q[0:1], k[0:1], v[0:1])
+    assert np.array_equal(out[0:1], o0) and np.array_equal(lse[0:1], l0)
+    assert np.all(out[2] == 0.0) and np.all(lse[2] == -np.inf)
+    rows = np.array([0, 5, 89])
+    orow, lrow = impl.cross_attention(q, k, v, kv_lens=lens, rows=rows)
+    assert np.max(np.abs(orow - out[:, :, rows])) < 1e-12
+    assert np.array_equal(lrow == -np.inf, lse[:, :, rows] == -np.inf)
+    fin = np.isfinite(lrow)
+    assert np.max(np.abs(lrow[fin] - lse[:, :, rows][fin])) < 1e-12
+
+
+def pin_cross_brute_force(impl):
+    """A few rows against a pure-Python attention with math.fsum (text length 9, padding 3)."""
+    rng = np.random.default_rng(63)
+    q = rng.standard_normal((1, 1, 5, 64))
+    k = rng.standard_normal((1, 1, 12, 64))
+    v = rng.standard_normal((1, 1, 12, 64))
+    out, lse = impl.cross_attention(q, k, v, kv_lens=[9])
+    for r in range(5):
+        ro, rl = _brute_attention_row(q[0, 0, r].tolist(), k[0, 0].tolist(), v[0, 0].tolist(),
+                                      [c < 9 for c in range(12)])
+        assert np.max(np.abs(out[0, 0, r] - ro)) < 1e-12
+        assert abs(lse[0, 0, r] - rl) < 1e-12
+
+
 ALL_PINS = [
     pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
@@ -513,5 +572,5 @@ ALL_PINS = [
     pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_empty_row,
     pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
-    pin_backward_sampled_match_full,
+    pin_backward_sampled_match_full, pin_cross_dense_sdpa, pin_cross_padding, pin_cross_brute_force,
 ]

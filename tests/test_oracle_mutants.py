@@ -38,6 +38,13 @@ MUTANTS = {
                          "lse = np.where(empty, -np.inf, np.log(l_safe))")],
     "scores_use_v": [("s = (q @ k.T) * SOFTMAX_SCALE", "s = (q @ v.T) * SOFTMAX_SCALE")],
     "no_normalisation": [("out = (e @ v) / l_safe[:, None]", "out = (e @ v)")],
+    "cross_padding_inclusive": [("mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (rows.size, n_kv))",
+                                 "mask = np.broadcast_to(np.arange(n_kv)[None, :] <= length, (rows.size, n_kv))")],
+    "cross_padding_ignored": [("length = n_kv if kv_lens is None else int(kv_lens[b])", "length = n_kv")],
+    "cross_lens_of_first_item": [("length = n_kv if kv_lens is None else int(kv_lens[b])",
+                                  "length = n_kv if kv_lens is None else int(kv_lens[0])")],
+    "cross_rows_ignored": [("out[b, h], lse[b, h] = masked_attention(q[b, h, rows], k[b, h], v[b, h], mask)",
+                            "out[b, h], lse[b, h] = masked_attention(q[b, h, :rows.size], k[b, h], v[b, h], mask)")],
     "pairs_count_cond": [("n_cond[:, None] * n_cond[None, :]", "n_cond[:, None] * size[None, :]")],
     "cached_kv_order": [("k_full = np.concatenate([np.asarray(k_cond, np.float64), np.asarray(k_noise, np.float64)], axis=2)",
                          "k_full = np.concatenate([np.asarray(k_noise, np.float64), np.asarray(k_cond, np.float64)], axis=2)")],
