@@ -146,6 +146,22 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
                       f"(fp64 numpy oracle: RoPE + masked dense attention), {dt:.2f} s"}
 
 
+def timed_launches(torch, stream, launch, count: int) -> float:
+    """Average milliseconds per launch of `count` back-to-back launches, timed with HIP events
+    on the launch stream.  The GPU is first held busy by a spin kernel (~20 ms) while the host
+    queues every launch, so the events measure the kernels and not the host's launch rate
+    (short kernels would otherwise wait for Python between launches)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(40_000_000)
+    a.record(stream)
+    for _ in range(count):
+        launch()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / count
+
+
 def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
     """The QK prologue (RMSNorm of each head's channels + 3D-RoPE) on this workload's Q and
     K, timed apart from the attention step: HBM-bound, algorithmic bytes = bf16 read + write
@@ -158,28 +174,16 @@ def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
         bsa.qk_rmsnorm_rope3d(q, gq, 1e-6, w.grid, out=qn)
         bsa.qk_rmsnorm_rope3d(k, gk, 1e-6, w.grid, out=kn)
     torch.cuda.synchronize()
-    # back-to-back launches between two events (per-launch events would add the host's
-    # launch latency whenever the queue runs dry)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
+    def both():
         bsa.qk_rmsnorm_rope3d(q, gq, 1e-6, w.grid, out=qn)
         bsa.qk_rmsnorm_rope3d(k, gk, 1e-6, w.grid, out=kn)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / (2 * steps)
+    ms = timed_launches(torch, stream, both, steps) / 2
     nbytes = 4.0 * q.numel()
     gbps = nbytes / (ms * 1e-3) / 1e9
     # a plain device copy of the same tensor: the HBM rate a read + write stream reaches here
     for _ in range(3):
         qn.copy_(q)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        qn.copy_(q)
-    b.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = nbytes / (a.elapsed_time(b) / steps * 1e-3) / 1e9
+    copy_gbps = nbytes / (timed_launches(torch, stream, lambda: qn.copy_(q), steps) * 1e-3) / 1e9
     log(f"[bench] QK prologue: {ms:.4f} ms per tensor, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBS:.1f}% of HBM; "
         f"a plain copy of the tensor: {copy_gbps:.0f} GB/s)")
     del qn, kn
@@ -203,14 +207,9 @@ def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: in
     ws = torch.empty(2 * q.shape[0] * q.shape[1] * q.shape[2], dtype=torch.float32, device="cuda")
     for _ in range(3):
         bsa.backward(q, k, v, out, lse, do, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        bsa.backward(q, k, v, out, lse, do, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    ms = timed_launches(torch, stream,
+                        lambda: bsa.backward(q, k, v, out, lse, do, layout, dq=dq, dk=dk, dv=dv, workspace=ws),
+                        steps)
     eff = 2.5 * fwd_flops / (ms * 1e-3) / 1e12
     executed = 3.5 * fwd_flops / (ms * 1e-3) / 1e12
     log(f"[bench] backward: {ms:.3f} ms, {eff:.1f} TFLOP/s effective (2.5x forward FLOPs), "
@@ -221,6 +220,32 @@ def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: in
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / MFMA_BF16_PEAK_TFLOPS, 4),
             "executed_tflops": round(executed, 3), "launches": steps,
             "what": "dQ, dK, dV of the block-sparse attention (D = rowsum(dO*O) pass, query walk, key walk)"}
+
+
+def measure_cross(bsa, torch, q, w, steps: int, stream) -> dict:
+    """Cross-attention of this workload's video queries over 512 text tokens (32 heads), timed
+    apart from the self-attention step: algorithmic FLOPs = 4 * 64 * N * L * heads (dense)."""
+    from lcv_inputs import TEXT_LEN
+    gen = torch.Generator(device="cpu").manual_seed(14)
+    shape = (q.shape[0], q.shape[1], TEXT_LEN, 64)
+    k = torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
+    v = torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        bsa.cross_attention(q, k, v, out=out, lse=lse)
+    ms = timed_launches(torch, stream, lambda: bsa.cross_attention(q, k, v, out=out, lse=lse), steps)
+    flops = 4.0 * 64 * q.shape[2] * TEXT_LEN * q.shape[1] * q.shape[0]
+    tf = flops / (ms * 1e-3) / 1e12
+    nbytes = 2.0 * (2 * q.numel() + 2 * k.numel()) + 4.0 * lse.numel()
+    log(f"[bench] cross-attention ({TEXT_LEN} text tokens): {ms:.4f} ms, {tf:.1f} TFLOP/s "
+        f"({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% of MFMA peak; {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s of Q, O, K, V, lse)")
+    del k, v, out, lse
+    return {"bound": "mfma", "kernel": "bsa_fwd_kernel<cross>", "ms": round(ms, 4), "text_tokens": TEXT_LEN,
+            "flops": flops, "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "min_bytes": nbytes,
+            "hbm_gbs_at_min_bytes": round(nbytes / (ms * 1e-3) / 1e9, 1), "launches": steps,
+            "what": "video queries over 512 padded text tokens, dense softmax attention"}
 
 
 def main() -> int:
@@ -238,6 +263,8 @@ def main() -> int:
                     help="skip the separate measurement of the QK prologue (RMSNorm + 3D-RoPE) kernel")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate measurement of the attention backward")
+    ap.add_argument("--no-cross", action="store_true",
+                    help="skip the separate measurement of the cross-attention over text tokens")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
     ap.add_argument("--copy-calibration", action="store_true",
@@ -365,6 +392,8 @@ def main() -> int:
         result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
     if not args.no_backward:
         result["backward"] = measure_backward(bsa, torch, q, k, v, layout, w, flops, args.steps, stream)
+    if not args.no_cross:
+        result["cross_attention"] = measure_cross(bsa, torch, q, w, args.steps, stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 # Every symbol include/lcv_bsa.h declares.
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
             "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d", "lcv_bsa_forward",
-            "lcv_bsa_forward_cached", "lcv_bsa_backward", "lcv_last_error", "lcv_abi_version")
+            "lcv_bsa_forward_cached", "lcv_bsa_backward", "lcv_cross_attention", "lcv_last_error",
+            "lcv_abi_version")
 
 
 class LayoutParams(ctypes.Structure):
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "lcv_bsa_forward_cached": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid),
                                          vp, vp, vp]),
         "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp]),
+        "lcv_cross_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
         "lcv_last_error": (ctypes.c_char_p, []),
         "lcv_abi_version": (i32, []),
     }
@@ -296,3 +298,25 @@ def backward(q, k, v, out, lse, dout, layout: Layout, dq=None, dk=None, dv=None,
                                   _bf16(dout, "dout"), B, Hh, layout.handle, layout.cond_len, _bf16(dq, "dq"),
                                   _bf16(dk, "dk"), _bf16(dv, "dv"), workspace.data_ptr(), _stream_ptr(stream)))
     return dq, dk, dv
+
+
+def cross_attention(q, k, v, kv_lens=None, out=None, lse=None, with_lse: bool = True, stream=None):
+    """Cross-attention of video queries q [B, H, N, 64] over text keys/values k, v [B, H, L, 64]
+    (bf16); kv_lens: optional int32 CUDA tensor [B] of valid text lengths.  Returns (out, lse)."""
+    import torch
+    B, Hh, N, D = q.shape
+    if D != 64 or k.shape[:2] != (B, Hh) or k.shape[3] != 64 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, N, 64] and k, v [B, H, L, 64]")
+    L = k.shape[2]
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B
+                                or not kv_lens.is_contiguous()):
+        raise ValueError("kv_lens must be a contiguous int32 CUDA tensor of B values")
+    out = torch.empty_like(q) if out is None else out
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    _check(lib().lcv_cross_attention(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), B, Hh, N, L,
+                                     None if kv_lens is None else kv_lens.data_ptr(), _bf16(out, "out"),
+                                     None if lse is None else lse.data_ptr(), _stream_ptr(stream)))
+    return out, lse

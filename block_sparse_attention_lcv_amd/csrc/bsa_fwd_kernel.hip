@@ -109,27 +109,31 @@ static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <bool CACHED>
+// Row `key` (clamped to the last valid key, key_end - 1) of a K or V tensor.  Self-attention:
+// [BH, N, 64], split at kv_split between the condition cache and the noise tensor in the
+// cached call.  Cross-attention: the text tensor [BH, kv_len, 64].
+template <bool CACHED, bool CROSS>
 __device__ __forceinline__ const uint16_t* kv_row(const FwdParams& P, const uint16_t* cond, const uint16_t* noise,
-                                                 int bh, int key) {
-  key = key < P.N ? key : P.N - 1;
+                                                 int bh, int key, int key_end) {
+  key = key < key_end ? key : key_end - 1;
+  if constexpr (CROSS) return noise + ((int64_t)bh * P.kv_len + key) * 64;
   if (CACHED && key < P.kv_split) return cond + ((int64_t)bh * P.kv_split + key) * 64;
   return noise + ((int64_t)bh * (P.N - P.kv_split) + (key - P.kv_split)) * 64;
 }
 
 // Issue the asynchronous global -> LDS copies of block j into a stage's K and V tiles (V
 // always, K too unless K is rotated on the way); K chunks to be rotated are loaded into kreg.
-template <bool ROPE_K, bool CACHED>
+template <bool ROPE_K, bool CACHED, bool CROSS>
 __device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* kdst, unsigned char* vdst, int bh, int j,
-                                            int wave, int lane, u32x4 (&kreg)[kLoadsPerWave]) {
+                                            int key_end, int wave, int lane, u32x4 (&kreg)[kLoadsPerWave]) {
   const int gch = (lane & 7) ^ swz(lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
     const int key = 64 * j + 8 * u + (lane >> 3);
-    const uint16_t* vsrc = kv_row<CACHED>(P, P.v_cond, P.v, bh, key) + 8 * gch;
+    const uint16_t* vsrc = kv_row<CACHED, CROSS>(P, P.v_cond, P.v, bh, key, key_end) + 8 * gch;
     __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + 1024 * u), 16, 0, 0);
-    const uint16_t* ksrc = kv_row<CACHED>(P, P.k_cond, P.k, bh, key) + 8 * gch;
+    const uint16_t* ksrc = kv_row<CACHED, CROSS>(P, P.k_cond, P.k, bh, key, key_end) + 8 * gch;
     if constexpr (ROPE_K)
       kreg[c] = *reinterpret_cast<const u32x4*>(ksrc);
     else
@@ -211,8 +215,12 @@ __device__ __forceinline__ u32x4 scale_chunk(u32x4 raw) {
   return raw;
 }
 
-template <bool ROPE_Q, bool ROPE_K, bool CACHED>
+// CROSS: cross-attention of the video queries over text keys/values [BH, kv_len, 64]: every
+// query block attends every text block (dense, no RoPE, no condition rule), keys past the
+// batch item's text length are masked.
+template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const FwdParams P) {
+  static_assert(!CROSS || (!ROPE_Q && !ROPE_K && !CACHED), "cross-attention has no RoPE and no cache");
   // LDS: the K and V tiles of stages 0 and 1 are four separate variables, so the compiler
   // can tell that reads of one stage do not depend on the global -> LDS copies into the
   // other (with one shared array it makes those reads wait for every copy in flight); the
@@ -234,6 +242,16 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   if (item >= P.n_items) return;
   const int bh = item / P.n_st_active;
   const int st = P.st_first + (item - bh * P.n_st_active);
+  // keys [0, key_end) exist: the sequence (self-attention) or the batch item's text length
+  int key_end = P.N;
+  if constexpr (CROSS) {
+    key_end = P.kv_len;
+    if (P.kv_lens != nullptr) {
+      const int len = P.kv_lens[bh / P.heads];
+      key_end = len < 0 ? 0 : (len < P.kv_len ? len : P.kv_len);
+    }
+    key_end = __builtin_amdgcn_readfirstlane(key_end);
+  }
 
   // ---- cos/sin table of every (axis, position, pair) of the grid
   float2* tab = reinterpret_cast<float2*>(smem);
@@ -308,18 +326,26 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   float lsum[2] = {0.f, 0.f};
   bf16x8 mneg[2] = {fold_operand(0.f, g), fold_operand(0.f, g)};
 
-  const int32_t* ents = P.st_ent + P.row_ptr[st * kWaves];
-  const int cnt = P.st_cnt[st];
+  // the workgroup's list: layout-built (self-attention), or every text block for all four
+  // wavefronts (cross-attention)
+  const int32_t* ents = CROSS ? nullptr : P.st_ent + P.row_ptr[st * kWaves];
+  const int cnt = CROSS ? (key_end + 63) >> 6 : P.st_cnt[st];
+  auto entry = [&](int e) __attribute__((always_inline)) {
+    if constexpr (CROSS)
+      return (e << 8) | ((1 << kWaves) - 1);
+    else
+      return ents[e];
+  };
 
   // List entries are wave-uniform (SGPRs): entry e+1 is known when step e starts (its block
   // is copied during step e) and entry e+2 is loaded during step e.
   u32x4 kreg[kLoadsPerWave];
   int ent_cur = 0, ent_next = 0;
   if (cnt > 0) {
-    ent_cur = __builtin_amdgcn_readfirstlane(ents[0]);
-    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(ents[1]);
+    ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
+    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
     const int j0 = ent_cur >> 8;
-    stage_issue<ROPE_K, CACHED>(P, lds_k0, lds_v0, bh, j0, wave, lane, kreg);
+    stage_issue<ROPE_K, CACHED, CROSS>(P, lds_k0, lds_v0, bh, j0, key_end, wave, lane, kreg);
     if constexpr (ROPE_K) stage_store_k(P, lds_k0, j0, wave, lane, tab, kreg);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -352,7 +378,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = key < P.N && (qtok[qt] >= P.C || key < P.C);
+        const bool ok = key < key_end && (qtok[qt] >= P.C || key < P.C);
         if (!ok) s[qt][r] = -INFINITY;
       }
   };
@@ -479,13 +505,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     // copies of block e+1 into the other stage; past the end of the list they re-read block
     // 0 into that stage, which nothing reads any more
     auto copies = [&]() __attribute__((always_inline)) {
-      stage_issue<ROPE_K, CACHED>(P, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, bh, jn, wave, lane, kreg);
+      stage_issue<ROPE_K, CACHED, CROSS>(P, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, bh, jn, key_end, wave,
+                                         lane, kreg);
     };
     // in flight until the barrier below (all lanes load the same entry)
-    const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
+    const int ent_after_raw = (e + 2 < cnt) ? entry(e + 2) : 0;
     if (wave_on && ((ent >> wave) & 1)) {
       const int j = ent >> 8;
-      bool need_mask = 64 * j + 63 >= P.N;
+      bool need_mask = 64 * j + 63 >= key_end;
       if constexpr (!CACHED) need_mask = need_mask || (64 * qblk < P.C && 64 * j + 63 >= P.C);
       if (need_mask)
         attend(stage_tag, std::true_type{}, j, copies);
@@ -533,9 +560,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   }
 }
 
-template <bool ROPE_Q, bool ROPE_K, bool CACHED>
+template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS = false>
 hipError_t launch_variant(const FwdParams& p, unsigned groups, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((bsa_fwd_kernel<ROPE_Q, ROPE_K, CACHED>), dim3(groups), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((bsa_fwd_kernel<ROPE_Q, ROPE_K, CACHED, CROSS>), dim3(groups), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -557,6 +584,12 @@ hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
     case 6: return launch_variant<true, true, false>(p, groups, lds, stream);
     default: return launch_variant<true, true, true>(p, groups, lds, stream);
   }
+}
+
+hipError_t launch_cross_fwd(const FwdParams& p, hipStream_t stream) {
+  if (p.n_items == 0) return hipSuccess;
+  const unsigned groups = (unsigned)(((int64_t)p.n_items + 7) / 8 * 8);
+  return launch_variant<false, false, false, true>(p, groups, 0, stream);
 }
 
 }  // namespace lcv

@@ -427,6 +427,49 @@ lcv_status lcv_qk_rmsnorm_rope3d(const void* x, void* y, const float* gamma, flo
   return ok();
 }
 
+lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
+                               int32_t n_q, int32_t kv_len, const int32_t* kv_lens, void* out, float* lse,
+                               hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(LCV_ERR_NULL, "q, k, v and out are required");
+  if (batch < 1 || heads < 1) return fail(LCV_ERR_INVALID_ARG, "batch and heads must be >= 1 (got %d, %d)", batch, heads);
+  if (n_q < 0 || kv_len < 0) return fail(LCV_ERR_INVALID_ARG, "n_q and kv_len must be >= 0 (got %d, %d)", n_q, kv_len);
+  for (const void* t : {q, k, v, static_cast<const void*>(out)})
+    if (!aligned(t, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(LCV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (kv_lens != nullptr && !aligned(kv_lens, 4)) return fail(LCV_ERR_INVALID_ARG, "kv_lens must be 4-byte aligned");
+  const int64_t bh = (int64_t)batch * heads;
+  const int32_t n_blocks = (int32_t)(((int64_t)n_q + 63) / 64);
+  const int32_t n_st = (n_blocks + lcv::kWaves - 1) / lcv::kWaves;
+  const int64_t n_items = bh * n_st;
+  if (n_items >= (int64_t(1) << 31) - 8 || bh >= (int64_t(1) << 31))
+    return fail(LCV_ERR_UNSUPPORTED, "batch*heads*workgroups = %lld is too large", (long long)n_items);
+  if (n_q == 0) return ok();
+  lcv::FwdParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.N = n_q;
+  p.C = 0;
+  p.n_blocks = n_blocks;
+  p.q_row0 = 0;
+  p.q_rows = n_q;
+  p.kv_split = 0;
+  p.st_first = 0;
+  p.n_st_active = n_st;
+  p.n_items = (int32_t)n_items;
+  p.flags = 0;
+  p.kv_len = kv_len;
+  p.kv_lens = kv_lens;
+  p.heads = heads;
+  hipError_t e = lcv::launch_cross_fwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "cross-attention launch");
+  return ok();
+}
+
 lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
                             const void* dout, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
                             int32_t cond_len, void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {

@@ -155,6 +155,10 @@ struct FwdParams {
   FastDiv div_hw, div_w;
   float log2_theta;
   int32_t rope_entries;     // 8T + 12H + 12W when a RoPE flag is set
+  // cross-attention only: text keys/values [BH, kv_len, 64], optional per-batch lengths
+  int32_t kv_len;
+  const int32_t* kv_lens;   // [B] device, or nullptr (all kv_len)
+  int32_t heads;
 };
 
 struct BwdParams {
@@ -182,6 +186,7 @@ struct BwdParams {
 
 hipError_t launch_layout_build(const LayoutRule& L, const LayoutDev& d, hipStream_t stream);
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream);
+hipError_t launch_cross_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int64_t n_outer, int32_t n_tokens,
                          int32_t token_offset, int32_t H, int32_t W, float log2_theta, hipStream_t stream);
 hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream);

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 3
+#define LCV_BSA_ABI_VERSION 4
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -199,6 +199,23 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
                             const void* dout, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
                             int32_t cond_len, void* dq, void* dk, void* dv, float* workspace,
                             hipStream_t stream);
+
+/* Cross-attention of the video tokens over text states, the second attention of every DiT
+ * block (myzaker article, technical principles: each block has 3D self-attention,
+ * cross-attention and a SwiGLU feed-forward network): out = softmax(q k^T / 8) v, dense over
+ * the text tokens, no RoPE.
+ *   q, out   : bf16 [batch, heads, n_q, 64] (video queries; normalise them first with
+ *              lcv_qk_rmsnorm_rope3d and grid = NULL if the model does)
+ *   k, v     : bf16 [batch, heads, kv_len, 64] (projected text states, padded to kv_len)
+ *   kv_lens  : device int32 [batch] valid text tokens per batch item (keys at or past it are
+ *              padding and ignored; values are clamped to [0, kv_len]), or NULL for kv_len
+ *   lse      : fp32 [batch, heads, n_q] natural-log LSE of the scaled scores, or NULL
+ * A batch item with no valid text token gives out = 0 and lse = -inf.  Caller-owned memory,
+ * no allocation, asynchronous on stream, deterministic.  Errors: NULL, INVALID_ARG (sizes,
+ * alignment), UNSUPPORTED (sizes), HIP. */
+lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
+                               int32_t n_q, int32_t kv_len, const int32_t* kv_lens, void* out, float* lse,
+                               hipStream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* lcv_last_error(void);

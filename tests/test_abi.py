@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 3
+    assert bsa.lib().lcv_abi_version() == 4
 
 
 QUERY_CASES = [
@@ -100,6 +100,22 @@ def test_forward_requires_layout():
     assert L.lcv_bsa_layout_get_info(None, None) == 1
     assert L.lcv_bsa_layout_copy_csr(None, p, p, None) == 1
     L.lcv_bsa_layout_destroy(None)   # no-op
+
+
+def test_cross_attention_argument_errors():
+    L = bsa.lib()
+    p = ctypes.c_void_p(4096)
+    f = L.lcv_cross_attention
+    assert f(None, p, p, 1, 1, 64, 64, None, p, None, None) == 1
+    assert f(p, p, p, 1, 1, 64, 64, None, None, None, None) == 1
+    assert f(p, p, p, 0, 1, 64, 64, None, p, None, None) == 2
+    assert f(p, p, p, 1, 1, -1, 64, None, p, None, None) == 2
+    assert f(p, p, p, 1, 1, 64, -5, None, p, None, None) == 2
+    assert f(ctypes.c_void_p(4104), p, p, 1, 1, 64, 64, None, p, None, None) == 2
+    assert f(p, p, p, 1, 1, 64, 64, None, p, ctypes.c_void_p(4098), None) == 2
+    assert f(p, p, p, 1, 1, 64, 64, ctypes.c_void_p(4097), p, None, None) == 2
+    assert f(p, p, p, 1, 1, 0, 64, None, p, None, None) == 0          # no query: nothing to do
+    assert f(p, p, p, 65536, 65536, 64, 64, None, p, None, None) == 6
 
 
 def test_backward_argument_errors():
