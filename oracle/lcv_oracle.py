@@ -32,6 +32,10 @@ fusion or reordering beyond what that definition states:
   second attention of every DiT block  [myzaker article, technical principles: each block is
   3D self-attention, cross-attention and a SwiGLU feed-forward network]): dense softmax
   attention over the first kv_len[b] text tokens of each batch item (the rest is padding);
+* the merge of attention results computed over disjoint key sets (context-parallel ring
+  attention [myzaker article, technical principles: context-parallel ring block-sparse
+  attention for high resolution]): with L = log(sum_i exp(lse_i)), out = sum_i exp(lse_i - L)
+  out_i, which is softmax attention over the union of the sets;
 * the gradients of the attention with respect to q, k, v (the backward pass that LoRA
   training of the model needs  [myzaker article, technical principles: the LoRA-trained
   refinement expert; SimpleTuner quickstart "LongCat-Video Edit", LoRA training]) by the
@@ -323,6 +327,27 @@ def cross_attention(q, k, v, kv_lens=None, rows=None):
         mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (rows.size, n_kv))
         for h in range(heads):
             out[b, h], lse[b, h] = masked_attention(q[b, h, rows], k[b, h], v[b, h], mask)
+    return out, lse
+
+
+def merge_partials(outs, lses):
+    """Merge attention results over disjoint key sets: outs [P][..., R, 64], lses [P][..., R]
+    (float64) -> out [..., R, 64], lse [..., R].  lse = log(sum_i exp(lse_i)) (taken around the
+    largest lse_i), out = sum_i exp(lse_i - lse) * out_i; rows where every part is empty
+    (all lse_i = -inf) give out = 0, lse = -inf."""
+    outs = [np.asarray(o, dtype=np.float64) for o in outs]
+    lses = [np.asarray(l, dtype=np.float64) for l in lses]
+    m = np.max(np.stack(lses), axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    weights = [np.exp(l - m_safe) for l in lses]
+    total = np.sum(np.stack(weights), axis=0)
+    total_safe = np.where(empty, 1.0, total)
+    out = np.zeros_like(outs[0])
+    for o, wgt in zip(outs, weights):
+        out += (wgt / total_safe)[..., None] * o
+    out[empty] = 0.0
+    lse = np.where(empty, -np.inf, m_safe + np.log(total_safe))
     return out, lse
 
 

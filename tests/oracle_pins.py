@@ -564,6 +564,40 @@ def pin_cross_brute_force(impl):
         assert abs(lse[0, 0, r] - rl) < 1e-12
 
 
+# ------------------------------------------------------------------------- partial merge
+def pin_merge_of_key_partition(impl):
+    """Softmax attention over a union of disjoint key sets equals the merge of the attention
+    over each set (the identity context-parallel attention relies on): three sets of a
+    block-sparse row mask (one of them empty for some rows), checked against the full
+    masked attention; merging one part returns it unchanged."""
+    rng = np.random.default_rng(71)
+    n = 200
+    q, k, v = (rng.standard_normal((n, 64)) for _ in range(3))
+    mask = impl.token_mask_rows(np.arange(n), n, 37, 1, 2)
+    key_set = np.where(np.arange(n) < 64, 1, 2 * rng.integers(0, 2, n))
+    # the 37 condition rows see keys < 37 only, all in set 1: sets 0 and 2 are empty for them
+    full_o, full_l = impl.masked_attention(q, k, v, mask)
+    parts = [impl.masked_attention(q, k, v, mask & (key_set == i)[None, :]) for i in range(3)]
+    assert np.any(~np.isfinite(parts[0][1]))    # some row sees none of set 0's keys
+    out, lse = impl.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    assert np.max(np.abs(out - full_o)) < 1e-12 and np.max(np.abs(lse - full_l)) < 1e-12
+    o1, l1 = impl.merge_partials([full_o], [full_l])
+    assert np.max(np.abs(o1 - full_o)) < 1e-15 and np.array_equal(l1, full_l)
+
+
+def pin_merge_closed_form(impl):
+    """Two parts with lse 0 and log 3 weigh 1/4 and 3/4 (lse log 4); an empty part (lse -inf)
+    weighs nothing; all parts empty give out = 0, lse = -inf."""
+    o_a = np.full((1, 64), 4.0)
+    o_b = np.full((1, 64), -8.0)
+    out, lse = impl.merge_partials([o_a, o_b], [np.array([0.0]), np.array([math.log(3.0)])])
+    assert np.max(np.abs(out - (0.25 * 4.0 + 0.75 * -8.0))) < 1e-14 and abs(lse[0] - math.log(4.0)) < 1e-15
+    out, lse = impl.merge_partials([o_a, o_b], [np.array([2.5]), np.array([-np.inf])])
+    assert np.array_equal(out, o_a) and lse[0] == 2.5
+    out, lse = impl.merge_partials([o_a, o_b], [np.array([-np.inf]), np.array([-np.inf])])
+    assert np.all(out == 0.0) and lse[0] == -np.inf
+
+
 ALL_PINS = [
     pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
@@ -573,4 +607,5 @@ ALL_PINS = [
     pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
     pin_backward_sampled_match_full, pin_cross_dense_sdpa, pin_cross_padding, pin_cross_brute_force,
+    pin_merge_of_key_partition, pin_merge_closed_form,
 ]

@@ -38,6 +38,10 @@ MUTANTS = {
                          "lse = np.where(empty, -np.inf, np.log(l_safe))")],
     "scores_use_v": [("s = (q @ k.T) * SOFTMAX_SCALE", "s = (q @ v.T) * SOFTMAX_SCALE")],
     "no_normalisation": [("out = (e @ v) / l_safe[:, None]", "out = (e @ v)")],
+    "merge_weight_not_normalised": [("out += (wgt / total_safe)[..., None] * o", "out += wgt[..., None] * o")],
+    "merge_lse_without_max": [("lse = np.where(empty, -np.inf, m_safe + np.log(total_safe))",
+                               "lse = np.where(empty, -np.inf, np.log(total_safe))")],
+    "merge_lse_mean": [("total = np.sum(np.stack(weights), axis=0)", "total = np.mean(np.stack(weights), axis=0)")],
     "cross_padding_inclusive": [("mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (rows.size, n_kv))",
                                  "mask = np.broadcast_to(np.arange(n_kv)[None, :] <= length, (rows.size, n_kv))")],
     "cross_padding_ignored": [("length = n_kv if kv_lens is None else int(kv_lens[b])", "length = n_kv")],
