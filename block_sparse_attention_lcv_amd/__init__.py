@@ -23,8 +23,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 # Every symbol include/lcv_bsa.h declares.
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
             "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d", "lcv_bsa_forward",
-            "lcv_bsa_forward_cached", "lcv_bsa_backward", "lcv_cross_attention", "lcv_last_error",
-            "lcv_abi_version")
+            "lcv_bsa_forward_cached", "lcv_bsa_backward", "lcv_cross_attention", "lcv_attn_merge",
+            "lcv_last_error", "lcv_abi_version")
 
 
 class LayoutParams(ctypes.Structure):
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp]),
         "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp]),
         "lcv_cross_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "lcv_attn_merge": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, vp, vp, vp]),
         "lcv_last_error": (ctypes.c_char_p, []),
         "lcv_abi_version": (i32, []),
     }
@@ -319,4 +320,32 @@ def cross_attention(q, k, v, kv_lens=None, out=None, lse=None, with_lse: bool = 
     _check(lib().lcv_cross_attention(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), B, Hh, N, L,
                                      None if kv_lens is None else kv_lens.data_ptr(), _bf16(out, "out"),
                                      None if lse is None else lse.data_ptr(), _stream_ptr(stream)))
+    return out, lse
+
+
+def attn_merge(outs, lses, out=None, lse=None, with_lse: bool = True, stream=None):
+    """Merge attention results over disjoint key sets: outs (bf16 [..., N, 64]) and lses
+    (float32 [..., N]) of each part -> (out, lse) of the attention over the union."""
+    import torch
+    if not 1 <= len(outs) <= 8 or len(lses) != len(outs):
+        raise ValueError("1 to 8 parts, one lse per out")
+    shape = outs[0].shape
+    if shape[-1] != 64:
+        raise ValueError("last dimension must be 64")
+    for o, l in zip(outs, lses):
+        if o.shape != shape or tuple(l.shape) != tuple(shape[:-1]):
+            raise ValueError("every part must have the same shape [..., N, 64] with lse [..., N]")
+        if l.dtype != torch.float32 or not l.is_cuda or not l.is_contiguous():
+            raise ValueError("lse parts must be contiguous float32 CUDA tensors")
+    out = torch.empty_like(outs[0]) if out is None else out
+    if out.shape != shape:
+        raise ValueError("out must have the parts' shape")
+    if with_lse and lse is None:
+        lse = torch.empty(shape[:-1], dtype=torch.float32, device=outs[0].device)
+    rows = outs[0].numel() // 64
+    n = len(outs)
+    optr = (ctypes.c_void_p * n)(*[_bf16(o, "outs[i]") for o in outs])
+    lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
+    _check(lib().lcv_attn_merge(optr, lptr, n, rows, _bf16(out, "out"), None if lse is None else lse.data_ptr(),
+                                _stream_ptr(stream)))
     return out, lse

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 4
+#define LCV_BSA_ABI_VERSION 5
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -216,6 +216,21 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
 lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
                                int32_t n_q, int32_t kv_len, const int32_t* kv_lens, void* out, float* lse,
                                hipStream_t stream);
+
+/* Merge of attention results over disjoint key sets, the combine step of context-parallel
+ * ring attention (myzaker article, technical principles: context-parallel ring block-sparse
+ * attention): lse = log(sum_i exp(lse_i)), out = sum_i exp(lse_i - lse) * out_i, the
+ * attention over the union of the sets.
+ *   outs     : host array of n_parts device pointers, bf16 [rows, 64] each (rows = B*H*N)
+ *   lses     : host array of n_parts device pointers, fp32 [rows] each (natural-log LSE;
+ *              -inf marks a row with no key in that part)
+ *   n_parts  : 1 .. 8
+ *   out, lse : bf16 [rows, 64] and fp32 [rows] (lse may be NULL); may be outs[i] / lses[i]
+ *              (in-place merge)
+ * A row empty in every part gives out = 0, lse = -inf.  fp32 math, one bf16 rounding.
+ * Asynchronous on stream.  Errors: NULL, INVALID_ARG (sizes, alignment), UNSUPPORTED, HIP. */
+lcv_status lcv_attn_merge(const void* const* outs, const float* const* lses, int32_t n_parts, int64_t rows,
+                          void* out, float* lse, hipStream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* lcv_last_error(void);

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 4
+    assert bsa.lib().lcv_abi_version() == 5
 
 
 QUERY_CASES = [
@@ -116,6 +116,24 @@ def test_cross_attention_argument_errors():
     assert f(p, p, p, 1, 1, 64, 64, ctypes.c_void_p(4097), p, None, None) == 2
     assert f(p, p, p, 1, 1, 0, 64, None, p, None, None) == 0          # no query: nothing to do
     assert f(p, p, p, 65536, 65536, 64, 64, None, p, None, None) == 6
+
+
+def test_merge_argument_errors():
+    L = bsa.lib()
+    p = ctypes.c_void_p(4096)
+    arr = (ctypes.c_void_p * 2)(4096, 8192)
+    bad = (ctypes.c_void_p * 2)(4096, 4100)
+    null_part = (ctypes.c_void_p * 2)(4096, None)
+    f = L.lcv_attn_merge
+    assert f(None, arr, 2, 10, p, None, None) == 1
+    assert f(arr, arr, 2, 10, None, None, None) == 1
+    assert f(arr, null_part, 2, 10, p, None, None) == 1
+    assert f(arr, arr, 0, 10, p, None, None) == 2
+    assert f(arr, arr, 9, 10, p, None, None) == 2
+    assert f(arr, arr, 2, -1, p, None, None) == 2
+    assert f(bad, arr, 2, 10, p, None, None) == 2
+    assert f(arr, arr, 2, 10, p, ctypes.c_void_p(4098), None) == 2
+    assert f(arr, arr, 2, 0, p, None, None) == 0          # no rows: nothing to do
 
 
 def test_backward_argument_errors():
