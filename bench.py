@@ -248,6 +248,48 @@ def measure_cross(bsa, torch, q, w, steps: int, stream) -> dict:
             "what": "video queries over 512 padded text tokens, dense softmax attention"}
 
 
+def measure_merge(bsa, torch, q, steps: int, stream) -> dict:
+    """The merge of two partial attention results of this workload's shape (the combine step
+    of ring attention over two key shards), HBM-bound: algorithmic bytes = both parts' bf16
+    out and fp32 lse read, the merged out and lse written."""
+    gen = torch.Generator(device="cpu").manual_seed(15)
+    outs = [torch.randn(q.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda() for _ in range(2)]
+    lses = [(torch.rand(q.shape[:3], generator=gen) * 10).cuda() for _ in range(2)]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        bsa.attn_merge(outs, lses, out=out, lse=lse)
+    ms = timed_launches(torch, stream, lambda: bsa.attn_merge(outs, lses, out=out, lse=lse), steps)
+    nbytes = 3.0 * (2 * q.numel() + 4 * lse.numel())
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] merge of 2 partial results: {ms:.4f} ms, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBS:.1f}% of HBM)")
+    del outs, lses, out, lse
+    return {"bound": "hbm", "kernel": "attn_merge_kernel", "avg_launch_ms": round(ms, 4), "bytes_per_launch": nbytes,
+            "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+            "launches": steps, "what": "merge of two partial attention results (bf16 out + fp32 lse each)"}
+
+
+def attended_pairs_from(n_tokens: int, cond: int, local: int, stride: int, q_from: int) -> int:
+    """Attended (query, key) token pairs of the query rows q >= q_from, counted per block pair
+    of the layout rule: a noise row sees every key of an allowed block, a condition row only
+    the block's condition keys (host arithmetic for the FLOP count of the cached call)."""
+    n = -(-n_tokens // 64)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    mb = np.abs(i - j) <= local
+    if stride >= 1:
+        mb = mb | (j % stride == 0)
+    blk_lo = np.arange(n, dtype=np.int64) * 64
+    blk_hi = np.minimum(blk_lo + 64, n_tokens)
+    lo = np.maximum(blk_lo, q_from)
+    noise_rows = np.clip(blk_hi - np.maximum(lo, cond), 0, None)
+    cond_rows = np.clip(np.minimum(blk_hi, cond) - lo, 0, None)
+    keys_all = blk_hi - blk_lo
+    keys_cond = np.clip(np.minimum(blk_hi, cond) - blk_lo, 0, None)
+    return int((noise_rows[:, None] * (mb * keys_all[None, :])).sum()
+               + (cond_rows[:, None] * (mb * keys_cond[None, :])).sum())
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +300,11 @@ def main() -> int:
                     help="k-pass: K rotated by the standalone RoPE pass into a second buffer, Q rotated "
                          "inside the attention kernel (both timed); fused: Q and K rotated inside the "
                          "attention kernel; none: inputs taken as already rotated")
+    ap.add_argument("--cached", action="store_true",
+                    help="time the workload's second call: noise-token rows [C, N) with the condition K/V "
+                         "taken from the cache (workloads with condition frames)")
+    ap.add_argument("--local", type=int, default=None, help="override the layout's local window (blocks)")
+    ap.add_argument("--stride", type=int, default=None, help="override the layout's global stride")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip the separate measurement of the QK prologue (RMSNorm + 3D-RoPE) kernel")
@@ -265,6 +312,8 @@ def main() -> int:
                     help="skip the separate measurement of the attention backward")
     ap.add_argument("--no-cross", action="store_true",
                     help="skip the separate measurement of the cross-attention over text tokens")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="skip the separate measurement of the merge of partial attention results")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
     ap.add_argument("--copy-calibration", action="store_true",
@@ -285,8 +334,16 @@ def main() -> int:
     import torch
     import block_sparse_attention_lcv_amd as bsa
 
+    import dataclasses
     w = WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name}: grid {w.grid} N={w.n_tokens} heads={w.heads} C={w.cond_len}")
+    if args.local is not None or args.stride is not None:
+        w = dataclasses.replace(w, local_blocks=w.local_blocks if args.local is None else args.local,
+                                global_stride=w.global_stride if args.stride is None else args.stride)
+    if args.cached and w.cond_len == 0:
+        print(f"--cached needs a workload with condition frames ({w.name} has none)", file=sys.stderr)
+        return 2
+    log(f"[bench] workload {w.name}: grid {w.grid} N={w.n_tokens} heads={w.heads} C={w.cond_len} "
+        f"local {w.local_blocks} stride {w.global_stride}{' (cached second call)' if args.cached else ''}")
     torch.cuda.init()
     stream = torch.cuda.current_stream()
 
@@ -294,8 +351,12 @@ def main() -> int:
     layout = bsa.build_layout(w.n_tokens, w.local_blocks, w.global_stride, w.cond_len)
     layout_ms = (time.perf_counter() - t0) * 1e3
     info = layout.info
-    flops = 4.0 * 64 * info["attended_pairs"] * w.heads * w.batch
-    log(f"[bench] layout nnz={info['nnz']} pairs/head={info['attended_pairs']} build {layout_ms:.2f} ms")
+    pairs = info["attended_pairs"]
+    if args.cached:
+        pairs = attended_pairs_from(w.n_tokens, w.cond_len, w.local_blocks, w.global_stride, w.cond_len)
+    flops = 4.0 * 64 * pairs * w.heads * w.batch
+    log(f"[bench] layout nnz={info['nnz']} pairs/head={info['attended_pairs']} (timed rows: {pairs}) "
+        f"build {layout_ms:.2f} ms")
 
     qb, kb, vb = workload_inputs(w)
 
@@ -304,22 +365,36 @@ def main() -> int:
 
     q, k, v = dev(qb), dev(kb), dev(vb)
     del qb, kb, vb
+    C = w.cond_len
+    if args.cached:
+        # the cache: condition K (rotated unless the attention kernel rotates K) and V of call 1;
+        # call 2 brings fresh noise-token Q, K, V
+        v_cond = v[:, :, :C].contiguous()
+        k_cond = k[:, :, :C].contiguous()
+        if args.rope_mode == "k-pass":
+            k_cond = bsa.rope3d_apply(k_cond, w.grid)
+        qb, kb, vb = workload_inputs(w, call=1)
+        q, k, v = dev(qb), dev(kb), dev(vb)
+        del qb, kb, vb
     out = torch.empty_like(q)
-    lse = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     k_rot = torch.empty_like(k) if args.rope_mode == "k-pass" else None
+    k_offset = C if args.cached else 0
 
     # one step; ev_mid (if given) is recorded between the RoPE pass and the attention kernel
     def step(ev_mid=None):
         if args.rope_mode == "k-pass":
-            bsa.rope3d_apply(k, w.grid, out=k_rot)
+            bsa.rope3d_apply(k, w.grid, token_offset=k_offset, out=k_rot)
         if ev_mid is not None:
             ev_mid.record(stream)
-        if args.rope_mode == "k-pass":
-            bsa.forward(q, k_rot, v, layout, grid=w.grid, rope_q=True, rope_k=False, out=out, lse=lse)
-        elif args.rope_mode == "fused":
-            bsa.forward(q, k, v, layout, grid=w.grid, out=out, lse=lse)
+        grid = None if args.rope_mode == "none" else w.grid
+        kk = k_rot if args.rope_mode == "k-pass" else k
+        rk = args.rope_mode == "fused"
+        if args.cached:
+            bsa.forward_cached(q, kk, v, k_cond, v_cond, layout, grid=grid, rope_q=grid is not None, rope_k=rk,
+                               out=out, lse=lse)
         else:
-            bsa.forward(q, k, v, layout, grid=None, out=out, lse=lse)
+            bsa.forward(q, kk, v, layout, grid=grid, rope_q=grid is not None, rope_k=rk, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -350,6 +425,8 @@ def main() -> int:
         f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}); K RoPE pass avg {np.mean(rope_ms):.3f} ms; "
         f"{value:.1f} TFLOP/s effective per step")
 
+    default_config = (args.workload == "t2v720" and not args.cached and args.rope_mode == "k-pass"
+                      and args.local is None and args.stride is None)
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -372,6 +449,9 @@ def main() -> int:
                      "fused": "Q and K rotated in the attention kernel's loads",
                      "none": "none (inputs taken as rotated)"}[args.rope_mode],
             "nnz": info["nnz"], "attended_pairs_per_head": info["attended_pairs"],
+            "call": ("cached second call: noise rows [C, N), condition K/V from the cache"
+                     if args.cached else "full call"),
+            "timed_pairs_per_head": pairs,
             "effective_flops": flops,
         },
         "pct_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
@@ -382,18 +462,22 @@ def main() -> int:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_from_profile(args.traffic_json),
+            # the committed counter summary covers the default configuration only
+            "traffic": traffic_from_profile(args.traffic_json) if default_config else None,
             "kernel": "bsa_fwd_kernel",
             "avg_launch_ms": round(avg_launch_ms, 4),
         },
         "rope_pass_ms": round(float(np.mean(rope_ms)), 4) if args.rope_mode == "k-pass" else None,
     }
-    if not args.no_prologue:
+    # the other kernels are measured on the full call's tensors
+    if not args.no_prologue and not args.cached:
         result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
-    if not args.no_backward:
+    if not args.no_backward and not args.cached:
         result["backward"] = measure_backward(bsa, torch, q, k, v, layout, w, flops, args.steps, stream)
-    if not args.no_cross:
+    if not args.no_cross and not args.cached:
         result["cross_attention"] = measure_cross(bsa, torch, q, w, args.steps, stream)
+    if not args.no_merge and not args.cached:
+        result["merge"] = measure_merge(bsa, torch, q, args.steps, stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

@@ -109,31 +109,61 @@ static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Row `key` (clamped to the last valid key, key_end - 1) of a K or V tensor.  Self-attention:
-// [BH, N, 64], split at kv_split between the condition cache and the noise tensor in the
-// cached call.  Cross-attention: the text tensor [BH, kv_len, 64].
+// Where the rows of one (batch, head)'s keys and values live, as byte addresses of key row 0
+// (wave-uniform, computed once): key row `key` is at cond + 128 key when key < split (the
+// condition cache of the cached call), else at noise + 128 key.  Self-attention: the
+// [BH, N, 64] tensors (the noise tensor of the cached call holds rows [split, N), so its
+// address is taken split rows early); cross-attention: the text tensor [BH, kv_len, 64].
+struct KvSrc {
+  uint64_t k_cond, v_cond, k_noise, v_noise;
+  int split;      // 0 unless cached
+  int key_end;    // keys [0, key_end) exist; rows past it read the last one
+};
+
 template <bool CACHED, bool CROSS>
-__device__ __forceinline__ const uint16_t* kv_row(const FwdParams& P, const uint16_t* cond, const uint16_t* noise,
-                                                 int bh, int key, int key_end) {
-  key = key < key_end ? key : key_end - 1;
-  if constexpr (CROSS) return noise + ((int64_t)bh * P.kv_len + key) * 64;
-  if (CACHED && key < P.kv_split) return cond + ((int64_t)bh * P.kv_split + key) * 64;
-  return noise + ((int64_t)bh * (P.N - P.kv_split) + (key - P.kv_split)) * 64;
+__device__ __forceinline__ KvSrc kv_src(const FwdParams& P, int bh, int key_end) {
+  KvSrc s;
+  s.key_end = key_end;
+  s.split = CACHED ? P.kv_split : 0;
+  const int64_t rows = CROSS ? P.kv_len : P.N - s.split;            // rows per (batch, head) of the noise tensor
+  const int64_t noise0 = (int64_t)bh * rows - s.split;              // its row index of key 0
+  s.k_noise = (uint64_t)(uintptr_t)P.k + (uint64_t)(noise0 * 128);
+  s.v_noise = (uint64_t)(uintptr_t)P.v + (uint64_t)(noise0 * 128);
+  s.k_cond = CACHED ? (uint64_t)(uintptr_t)P.k_cond + (uint64_t)((int64_t)bh * s.split * 128) : 0;
+  s.v_cond = CACHED ? (uint64_t)(uintptr_t)P.v_cond + (uint64_t)((int64_t)bh * s.split * 128) : 0;
+  return s;
+}
+
+// Row `key` (clamped to key_end - 1) of K (is_k) or V, 16-byte chunk `chunk`; row0 is the
+// first key of the lane's 8-row group (wave-uniform): the source tensor is chosen per group,
+// per lane only in the group that holds the condition boundary.
+template <bool CACHED>
+__device__ __forceinline__ const uint16_t* kv_row(const KvSrc& s, bool is_k, int row0, int key, int chunk) {
+  key = key < s.key_end ? key : s.key_end - 1;
+  uint64_t base = is_k ? s.k_noise : s.v_noise;
+  if constexpr (CACHED) {
+    if (row0 < s.split) {
+      base = is_k ? s.k_cond : s.v_cond;
+      if (key >= s.split) base = is_k ? s.k_noise : s.v_noise;
+    }
+  }
+  return reinterpret_cast<const uint16_t*>(base + (uint64_t)key * 128 + 16 * chunk);
 }
 
 // Issue the asynchronous global -> LDS copies of block j into a stage's K and V tiles (V
 // always, K too unless K is rotated on the way); K chunks to be rotated are loaded into kreg.
-template <bool ROPE_K, bool CACHED, bool CROSS>
-__device__ __forceinline__ void stage_issue(const FwdParams& P, unsigned char* kdst, unsigned char* vdst, int bh, int j,
-                                            int key_end, int wave, int lane, u32x4 (&kreg)[kLoadsPerWave]) {
+template <bool ROPE_K, bool CACHED>
+__device__ __forceinline__ void stage_issue(const KvSrc& src, unsigned char* kdst, unsigned char* vdst, int j, int wave,
+                                            int lane, u32x4 (&kreg)[kLoadsPerWave]) {
   const int gch = (lane & 7) ^ swz(lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
     const int key = 64 * j + 8 * u + (lane >> 3);
-    const uint16_t* vsrc = kv_row<CACHED, CROSS>(P, P.v_cond, P.v, bh, key, key_end) + 8 * gch;
+    const int row0 = 64 * j + 8 * u;
+    const uint16_t* vsrc = kv_row<CACHED>(src, false, row0, key, gch);
     __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + 1024 * u), 16, 0, 0);
-    const uint16_t* ksrc = kv_row<CACHED, CROSS>(P, P.k_cond, P.k, bh, key, key_end) + 8 * gch;
+    const uint16_t* ksrc = kv_row<CACHED>(src, true, row0, key, gch);
     if constexpr (ROPE_K)
       kreg[c] = *reinterpret_cast<const u32x4*>(ksrc);
     else
@@ -252,6 +282,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     }
     key_end = __builtin_amdgcn_readfirstlane(key_end);
   }
+  const KvSrc kvs = kv_src<CACHED, CROSS>(P, bh, key_end);
 
   // ---- cos/sin table of every (axis, position, pair) of the grid
   float2* tab = reinterpret_cast<float2*>(smem);
@@ -345,7 +376,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
     if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
     const int j0 = ent_cur >> 8;
-    stage_issue<ROPE_K, CACHED, CROSS>(P, lds_k0, lds_v0, bh, j0, key_end, wave, lane, kreg);
+    stage_issue<ROPE_K, CACHED>(kvs, lds_k0, lds_v0, j0, wave, lane, kreg);
     if constexpr (ROPE_K) stage_store_k(P, lds_k0, j0, wave, lane, tab, kreg);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -505,15 +536,17 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     // copies of block e+1 into the other stage; past the end of the list they re-read block
     // 0 into that stage, which nothing reads any more
     auto copies = [&]() __attribute__((always_inline)) {
-      stage_issue<ROPE_K, CACHED, CROSS>(P, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, bh, jn, key_end, wave,
-                                         lane, kreg);
+      stage_issue<ROPE_K, CACHED>(kvs, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, jn, wave, lane, kreg);
     };
     // in flight until the barrier below (all lanes load the same entry)
     const int ent_after_raw = (e + 2 < cnt) ? entry(e + 2) : 0;
     if (wave_on && ((ent >> wave) & 1)) {
       const int j = ent >> 8;
-      bool need_mask = 64 * j + 63 >= key_end;
-      if constexpr (!CACHED) need_mask = need_mask || (64 * qblk < P.C && 64 * j + 63 >= P.C);
+      // token mask at the end of the keys and where the block pair crosses the condition
+      // boundary (in the cached call the masked rows are not computed: the test is kept the
+      // same in every variant because the register allocation of the cached one spilled
+      // inside the loop without it)
+      const bool need_mask = 64 * j + 63 >= key_end || (64 * qblk < P.C && 64 * j + 63 >= P.C);
       if (need_mask)
         attend(stage_tag, std::true_type{}, j, copies);
       else

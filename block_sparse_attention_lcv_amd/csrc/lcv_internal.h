@@ -187,6 +187,17 @@ struct BwdParams {
 hipError_t launch_layout_build(const LayoutRule& L, const LayoutDev& d, hipStream_t stream);
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_cross_fwd(const FwdParams& p, hipStream_t stream);
+
+constexpr int kMaxMergeParts = 8;
+struct MergeParams {
+  const uint16_t* outs[kMaxMergeParts];   // bf16 [rows, 64] per part
+  const float* lses[kMaxMergeParts];      // fp32 [rows] per part
+  uint16_t* out;
+  float* lse;                             // or nullptr
+  int64_t rows;
+  int32_t n_parts;
+};
+hipError_t launch_attn_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int64_t n_outer, int32_t n_tokens,
                          int32_t token_offset, int32_t H, int32_t W, float log2_theta, hipStream_t stream);
 hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream);
