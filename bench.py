@@ -303,6 +303,9 @@ def main() -> int:
     ap.add_argument("--cached", action="store_true",
                     help="time the workload's second call: noise-token rows [C, N) with the condition K/V "
                          "taken from the cache (workloads with condition frames)")
+    ap.add_argument("--shard-of", type=int, default=0, metavar="G",
+                    help="time one device's share of a sequence-sharded call: the middle one of G block-aligned "
+                         "query-row ranges (K/V of the whole sequence resident)")
     ap.add_argument("--local", type=int, default=None, help="override the layout's local window (blocks)")
     ap.add_argument("--stride", type=int, default=None, help="override the layout's global stride")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -339,6 +342,9 @@ def main() -> int:
     if args.local is not None or args.stride is not None:
         w = dataclasses.replace(w, local_blocks=w.local_blocks if args.local is None else args.local,
                                 global_stride=w.global_stride if args.stride is None else args.stride)
+    if args.shard_of and args.cached:
+        print("--shard-of and --cached are exclusive", file=sys.stderr)
+        return 2
     if args.cached and w.cond_len == 0:
         print(f"--cached needs a workload with condition frames ({w.name} has none)", file=sys.stderr)
         return 2
@@ -352,8 +358,15 @@ def main() -> int:
     layout_ms = (time.perf_counter() - t0) * 1e3
     info = layout.info
     pairs = info["attended_pairs"]
+    row0, row1 = 0, w.n_tokens
     if args.cached:
         pairs = attended_pairs_from(w.n_tokens, w.cond_len, w.local_blocks, w.global_stride, w.cond_len)
+    elif args.shard_of:
+        per = -(-w.n_blocks // args.shard_of) * 64
+        g = args.shard_of // 2
+        row0, row1 = g * per, min((g + 1) * per, w.n_tokens)
+        pairs = (attended_pairs_from(w.n_tokens, w.cond_len, w.local_blocks, w.global_stride, row0)
+                 - attended_pairs_from(w.n_tokens, w.cond_len, w.local_blocks, w.global_stride, row1))
     flops = 4.0 * 64 * pairs * w.heads * w.batch
     log(f"[bench] layout nnz={info['nnz']} pairs/head={info['attended_pairs']} (timed rows: {pairs}) "
         f"build {layout_ms:.2f} ms")
@@ -376,6 +389,9 @@ def main() -> int:
         qb, kb, vb = workload_inputs(w, call=1)
         q, k, v = dev(qb), dev(kb), dev(vb)
         del qb, kb, vb
+    q_full = q
+    if args.shard_of:
+        q = q[:, :, row0:row1].contiguous()
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     k_rot = torch.empty_like(k) if args.rope_mode == "k-pass" else None
@@ -393,6 +409,9 @@ def main() -> int:
         if args.cached:
             bsa.forward_cached(q, kk, v, k_cond, v_cond, layout, grid=grid, rope_q=grid is not None, rope_k=rk,
                                out=out, lse=lse)
+        elif args.shard_of:
+            bsa.forward_rows(q, kk, v, layout, row0, row1, grid=grid, rope_q=grid is not None, rope_k=rk,
+                             out=out, lse=lse)
         else:
             bsa.forward(q, kk, v, layout, grid=grid, rope_q=grid is not None, rope_k=rk, out=out, lse=lse)
 
@@ -425,8 +444,8 @@ def main() -> int:
         f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}); K RoPE pass avg {np.mean(rope_ms):.3f} ms; "
         f"{value:.1f} TFLOP/s effective per step")
 
-    default_config = (args.workload == "t2v720" and not args.cached and args.rope_mode == "k-pass"
-                      and args.local is None and args.stride is None)
+    default_config = (args.workload == "t2v720" and not args.cached and not args.shard_of
+                      and args.rope_mode == "k-pass" and args.local is None and args.stride is None)
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -449,8 +468,9 @@ def main() -> int:
                      "fused": "Q and K rotated in the attention kernel's loads",
                      "none": "none (inputs taken as rotated)"}[args.rope_mode],
             "nnz": info["nnz"], "attended_pairs_per_head": info["attended_pairs"],
-            "call": ("cached second call: noise rows [C, N), condition K/V from the cache"
-                     if args.cached else "full call"),
+            "call": ("cached second call: noise rows [C, N), condition K/V from the cache" if args.cached
+                     else f"rows [{row0}, {row1}): the middle of {args.shard_of} sequence shards" if args.shard_of
+                     else "full call"),
             "timed_pairs_per_head": pairs,
             "effective_flops": flops,
         },
@@ -470,13 +490,15 @@ def main() -> int:
         "rope_pass_ms": round(float(np.mean(rope_ms)), 4) if args.rope_mode == "k-pass" else None,
     }
     # the other kernels are measured on the full call's tensors
-    if not args.no_prologue and not args.cached:
+    q = q_full
+    extras = not args.cached and not args.shard_of
+    if not args.no_prologue and extras:
         result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
-    if not args.no_backward and not args.cached:
+    if not args.no_backward and extras:
         result["backward"] = measure_backward(bsa, torch, q, k, v, layout, w, flops, args.steps, stream)
-    if not args.no_cross and not args.cached:
+    if not args.no_cross and extras:
         result["cross_attention"] = measure_cross(bsa, torch, q, w, args.steps, stream)
-    if not args.no_merge and not args.cached:
+    if not args.no_merge and extras:
         result["merge"] = measure_merge(bsa, torch, q, args.steps, stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)

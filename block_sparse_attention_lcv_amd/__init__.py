@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 # Every symbol include/lcv_bsa.h declares.
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
             "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d", "lcv_bsa_forward",
-            "lcv_bsa_forward_cached", "lcv_bsa_backward", "lcv_cross_attention", "lcv_attn_merge",
+            "lcv_bsa_forward_cached", "lcv_bsa_forward_rows", "lcv_bsa_backward", "lcv_cross_attention", "lcv_attn_merge",
             "lcv_last_error", "lcv_abi_version")
 
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         "lcv_bsa_forward": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), vp, vp, vp]),
         "lcv_bsa_forward_cached": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid),
                                          vp, vp, vp]),
+        "lcv_bsa_forward_rows": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), i32, i32, vp, vp,
+                                       vp]),
         "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp]),
         "lcv_cross_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
         "lcv_attn_merge": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, vp, vp, vp]),
@@ -243,6 +245,28 @@ def forward(q, k, v, layout: Layout, grid=None, rope_q: bool = True, rope_k: boo
     _check(lib().lcv_bsa_forward(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), B, Hh, layout.handle,
                                  layout.cond_len, flags, ctypes.byref(g.c()) if g is not None else None,
                                  _bf16(out, "out"), lse_ptr, _stream_ptr(stream)))
+    return out, lse
+
+
+def forward_rows(q_rows, k, v, layout: Layout, row_begin: int, row_end: int, grid=None, rope_q: bool = True,
+                 rope_k: bool = True, out=None, lse=None, with_lse: bool = True, stream=None):
+    """Rows [row_begin, row_end) of forward(): q_rows [B, H, row_end - row_begin, 64], k, v the
+    full [B, H, N, 64] tensors.  Returns (out, lse) of the range's rows."""
+    import torch
+    B, Hh, M, D = q_rows.shape
+    if D != 64 or M != row_end - row_begin:
+        raise ValueError(f"q_rows must be [B, H, {row_end - row_begin}, 64]")
+    if k.shape != (B, Hh, layout.n_tokens, 64) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B, H, {layout.n_tokens}, 64]")
+    g = _as_grid(grid)
+    flags = _flags(rope_q, rope_k) if g is not None else 0
+    out = torch.empty_like(q_rows) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, M), dtype=torch.float32, device=q_rows.device)
+    _check(lib().lcv_bsa_forward_rows(_bf16(q_rows, "q_rows"), _bf16(k, "k"), _bf16(v, "v"), B, Hh, layout.handle,
+                                      layout.cond_len, flags, ctypes.byref(g.c()) if g is not None else None,
+                                      row_begin, row_end, _bf16(out, "out"), None if lse is None else lse.data_ptr(),
+                                      _stream_ptr(stream)))
     return out, lse
 
 

@@ -306,14 +306,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   // ---- this wavefront's query block as MFMA B operands: qf[qt][ks] holds rows
   // 32*qt + (lane & 31), channels 16*ks + 8*(lane >> 5) .. +7, scaled by log2(e)/8
   const int qblk = st * kWaves + wave;
-  const bool wave_on = (qblk < P.n_blocks) && (64 * qblk + 63 >= P.q_row0);
+  const bool wave_on = (qblk < P.n_blocks) && (64 * qblk + 63 >= P.q_row0) && (64 * qblk < P.q_end);
   bf16x8 qf[2][4];
   int qtok[2];
   bool qok[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     qtok[qt] = 64 * qblk + 32 * qt + l32;
-    qok[qt] = wave_on && qtok[qt] >= P.q_row0 && qtok[qt] < P.N;
+    qok[qt] = wave_on && qtok[qt] >= P.q_row0 && qtok[qt] < P.q_end;
     const uint16_t* qrow = P.q + ((int64_t)bh * P.q_rows + (qtok[qt] - P.q_row0)) * 64;
     Coords xyz{0u, 0u, 0u};
     if (ROPE_Q && qok[qt]) xyz = token_coords((uint32_t)qtok[qt], P);

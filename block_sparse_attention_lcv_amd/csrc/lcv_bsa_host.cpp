@@ -172,6 +172,8 @@ struct FwdArgs {
   void* out;
   float* lse;
   bool cached;
+  int32_t row_begin = 0;    // query rows [row_begin, row_end) of the call (row_end < 0: to N)
+  int32_t row_end = -1;
 };
 
 lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
@@ -211,11 +213,12 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
   }
   const int64_t bh = (int64_t)batch * heads;
   const int32_t n = info.n_blocks;
-  const int32_t q_row0 = a.cached ? C : 0;
-  if (q_row0 >= N) return ok();   // cached call with no noise tokens
+  const int32_t q_row0 = a.cached ? C : a.row_begin;
+  const int32_t q_end = a.row_end < 0 ? N : a.row_end;
+  if (q_row0 >= q_end) return ok();   // cached call with no noise tokens, or an empty row range
   const int32_t st_first = (q_row0 / 64) / lcv::kWaves;
-  const int32_t n_st = layout->dev.n_st;
-  const int64_t n_items = bh * (n_st - st_first);
+  const int32_t st_end = ((q_end + 63) / 64 + lcv::kWaves - 1) / lcv::kWaves;
+  const int64_t n_items = bh * (st_end - st_first);
   if (n_items >= (int64_t(1) << 31) - 8)
     return fail(LCV_ERR_UNSUPPORTED, "batch*heads*workgroups = %lld is too large", (long long)n_items);
 
@@ -241,10 +244,11 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
   p.C = C;
   p.n_blocks = n;
   p.q_row0 = q_row0;
-  p.q_rows = N - q_row0;
+  p.q_rows = q_end - q_row0;
+  p.q_end = q_end;
   p.kv_split = a.cached ? C : 0;
   p.st_first = st_first;
-  p.n_st_active = n_st - st_first;
+  p.n_st_active = st_end - st_first;
   p.n_items = (int32_t)n_items;
   p.flags = flags;
   if (flags) {
@@ -427,6 +431,33 @@ lcv_status lcv_qk_rmsnorm_rope3d(const void* x, void* y, const float* gamma, flo
   return ok();
 }
 
+lcv_status lcv_attn_merge(const void* const* outs, const float* const* lses, int32_t n_parts, int64_t rows,
+                          void* out, float* lse, hipStream_t stream) {
+  if (outs == nullptr || lses == nullptr || out == nullptr) return fail(LCV_ERR_NULL, "outs, lses and out are required");
+  if (n_parts < 1 || n_parts > lcv::kMaxMergeParts)
+    return fail(LCV_ERR_INVALID_ARG, "n_parts must be in [1, %d] (got %d)", lcv::kMaxMergeParts, n_parts);
+  if (rows < 0 || rows > (int64_t(1) << 40)) return fail(LCV_ERR_INVALID_ARG, "rows must be in [0, 2^40]");
+  lcv::MergeParams p;
+  std::memset(&p, 0, sizeof p);
+  for (int i = 0; i < n_parts; ++i) {
+    if (outs[i] == nullptr || lses[i] == nullptr) return fail(LCV_ERR_NULL, "part %d has a NULL pointer", i);
+    if (!aligned(outs[i], 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+    if (!aligned(lses[i], 4)) return fail(LCV_ERR_INVALID_ARG, "lse tensors must be 4-byte aligned");
+    p.outs[i] = static_cast<const uint16_t*>(outs[i]);
+    p.lses[i] = lses[i];
+  }
+  if (!aligned(out, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(LCV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (rows * 8 / 256 >= (int64_t(1) << 31)) return fail(LCV_ERR_UNSUPPORTED, "rows = %lld is too large", (long long)rows);
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.rows = rows;
+  p.n_parts = n_parts;
+  hipError_t e = lcv::launch_attn_merge(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
 lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
                                int32_t n_q, int32_t kv_len, const int32_t* kv_lens, void* out, float* lse,
                                hipStream_t stream) {
@@ -457,6 +488,7 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
   p.n_blocks = n_blocks;
   p.q_row0 = 0;
   p.q_rows = n_q;
+  p.q_end = n_q;
   p.kv_split = 0;
   p.st_first = 0;
   p.n_st_active = n_st;
@@ -529,6 +561,20 @@ lcv_status lcv_bsa_forward(const void* q, const void* k, const void* v, int32_t 
                            const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
                            const lcv_rope3d_grid* grid, void* out, float* lse, hipStream_t stream) {
   FwdArgs a{q, k, v, nullptr, nullptr, out, lse, false};
+  return forward_common(a, batch, heads, layout, cond_len, flags, grid, stream);
+}
+
+lcv_status lcv_bsa_forward_rows(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
+                                const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
+                                const lcv_rope3d_grid* grid, int32_t row_begin, int32_t row_end, void* out, float* lse,
+                                hipStream_t stream) {
+  if (layout != nullptr && (row_begin < 0 || row_end < row_begin || row_end > layout->info.n_tokens))
+    return fail(LCV_ERR_INVALID_ARG, "row range [%d, %d) is not inside [0, %d]", row_begin, row_end,
+                layout->info.n_tokens);
+  if (layout != nullptr && row_begin == row_end) return ok();   // empty range: nothing to read or write
+  FwdArgs a{q, k, v, nullptr, nullptr, out, lse, false};
+  a.row_begin = row_begin;
+  a.row_end = row_end;
   return forward_common(a, batch, heads, layout, cond_len, flags, grid, stream);
 }
 

@@ -145,7 +145,8 @@ struct FwdParams {
   const int32_t* st_ent;
   int32_t N, C, n_blocks;
   int32_t q_row0;           // first query token of the call (0 full, C cached)
-  int32_t q_rows;           // N - q_row0
+  int32_t q_rows;           // q_end - q_row0 (rows of the q, out and lse tensors)
+  int32_t q_end;            // one past the last query token of the call (N unless a row range)
   int32_t kv_split;         // keys < kv_split read from k_cond / v_cond
   int32_t st_first;         // first workgroup list used
   int32_t n_st_active;      // workgroup lists per (batch, head)

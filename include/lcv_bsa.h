@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 5
+#define LCV_BSA_ABI_VERSION 6
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -180,6 +180,19 @@ lcv_status lcv_bsa_forward_cached(const void* q_noise, const void* k_noise, cons
                                   const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
                                   const lcv_rope3d_grid* grid, void* out_noise, float* lse_noise,
                                   hipStream_t stream);
+
+/* Rows [row_begin, row_end) of lcv_bsa_forward: one device's share of a sequence-sharded call
+ * (context-parallel attention, myzaker article, technical principles: context-parallel
+ * block-sparse attention for high resolution).  q, out and lse hold only the range's rows
+ * ([batch, heads, row_end - row_begin, 64] and [batch, heads, row_end - row_begin]); k and v
+ * are the full [batch, heads, N, 64] tensors (on several devices, the gathered key/value
+ * blocks the range's rows attend to).  The rows' results are bitwise those of the full call.
+ * An empty range (row_begin == row_end) does nothing (its pointers may be NULL).
+ * Errors as lcv_bsa_forward, plus INVALID_ARG for a range outside [0, N]. */
+lcv_status lcv_bsa_forward_rows(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
+                                const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
+                                const lcv_rope3d_grid* grid, int32_t row_begin, int32_t row_end, void* out, float* lse,
+                                hipStream_t stream);
 
 /* Backward of lcv_bsa_forward (flags = 0): the gradients of the attention for the upstream
  * gradient dout, for training (myzaker article, technical principles: the LoRA-trained

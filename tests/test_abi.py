@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 5
+    assert bsa.lib().lcv_abi_version() == 6
 
 
 QUERY_CASES = [
@@ -99,6 +99,7 @@ def test_forward_requires_layout():
     assert L.lcv_bsa_forward_cached(p, p, p, p, p, 1, 1, None, 0, 3, ctypes.byref(g), p, None, None) == 1
     assert L.lcv_bsa_layout_get_info(None, None) == 1
     assert L.lcv_bsa_layout_copy_csr(None, p, p, None) == 1
+    assert L.lcv_bsa_forward_rows(p, p, p, 1, 1, None, 0, 3, ctypes.byref(g), 0, 64, p, None, None) == 1
     L.lcv_bsa_layout_destroy(None)   # no-op
 
 

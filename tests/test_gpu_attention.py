@@ -276,3 +276,49 @@ def test_vc_density_sweep(lib, local, stride):
     ww = _W()
     ww.heads, ww.grid, ww.cond_len, ww.theta = heads, w.grid, w.cond_len, w.theta
     _check_rows(out, lse, _oracle_rows_full(qb, kb, vb, ww, local, stride), rows, heads, f"sweep w{local} s{stride}")
+
+
+@pytest.mark.parametrize("name,grid,heads,cond,ranges", [
+    ("three-unaligned", (3, 10, 21), 2, 210, [(0, 200), (200, 413), (413, 630)]),
+    ("eight-aligned", (2, 16, 64), 2, 1061, [(256 * i, 256 * (i + 1)) for i in range(8)]),
+    ("single-rows", (1, 7, 9), 2, 5, [(0, 1), (1, 2), (2, 40), (40, 63)]),
+])
+def test_row_shards_match_full_bitwise(lib, name, grid, heads, cond, ranges):
+    """Sequence-sharded calls (one device's rows each) reproduce the full call bit for bit."""
+    import torch
+    say(f"[rows] {name}")
+    layout, _, (q, k, v), out, lse = _run_full(lib, grid, heads, cond, 2, 4, seed=37)
+    for r0, r1 in ranges:
+        o, l = lib.forward_rows(q[:, :, r0:r1].contiguous(), k, v, layout, r0, r1, grid=grid)
+        _sync()
+        assert torch.equal(o.view(torch.int16), out[:, :, r0:r1].view(torch.int16)), (r0, r1)
+        assert torch.equal(l, lse[:, :, r0:r1]), (r0, r1)
+    empty = torch.empty((1, heads, 0, 64), dtype=torch.bfloat16, device="cuda")
+    mid = layout.n_tokens // 2
+    lib.forward_rows(empty, k, v, layout, mid, mid, grid=grid)
+    import ctypes
+    p = ctypes.c_void_p(4096)
+    g = lib.Rope3dGrid(*grid, 1e4)
+    assert lib.lib().lcv_bsa_forward_rows(p, p, p, 1, heads, layout.handle, cond, 3, ctypes.byref(g), 5, 4, p, None,
+                                          None) == 2
+    assert lib.lib().lcv_bsa_forward_rows(p, p, p, 1, heads, layout.handle, cond, 3, ctypes.byref(g), 0,
+                                          layout.n_tokens + 1, p, None, None) == 2
+    layout.close()
+
+
+def test_row_shard_workload_bitwise(lib):
+    """One eighth of the 720p rows (the middle shard) against the same rows of the full call."""
+    import torch
+    w = WORKLOADS["t2v720"]
+    say("[rows] t2v720 shard 4 of 8")
+    qb, kb, vb = workload_inputs(w)
+    layout = lib.build_layout(w.n_tokens, w.local_blocks, w.global_stride, w.cond_len)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    out, lse = lib.forward(q, k, v, layout, grid=w.grid)
+    per = -(-w.n_blocks // 8) * 64
+    r0, r1 = 4 * per, min(5 * per, w.n_tokens)
+    o, l = lib.forward_rows(q[:, :, r0:r1].contiguous(), k, v, layout, r0, r1, grid=w.grid)
+    _sync()
+    assert torch.equal(o.view(torch.int16), out[:, :, r0:r1].view(torch.int16))
+    assert torch.equal(l, lse[:, :, r0:r1])
+    layout.close()
