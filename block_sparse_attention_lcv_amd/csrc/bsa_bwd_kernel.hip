@@ -7,18 +7,19 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D) with D = rowsum(dO * O),
 //   dQ = dS K / 8, dK = dS^T Q / 8.
 // Three kernels:
-//  * bwd_prep_kernel: D and 8 * lse per row (HBM-bound, one pass over O and dO);
+//  * bwd_prep_kernel: D and lse * log2(e) per row (HBM-bound, one pass over O and dO);
 //  * bwd_dq_kernel: the row walk of the forward -- a workgroup of 8 wavefronts owns 4 query
 //    blocks (32 rows per wavefront) and streams the K and V blocks of their rows through LDS;
 //    per 32-key half it forms S^T = K Q^T and dP^T = V dO^T with v_mfma_f32_32x32x16_bf16
-//    (8 * lse and D folded into one extra MFMA step each, as the forward folds its row max),
-//    then dS^T and dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16;
+//    (D folded into one extra MFMA step, as the forward folds its row max; the row's lse is
+//    the lane's own and enters through the FMA that scales the score), then dS^T and
+//    dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16;
 //  * bwd_dkdv_kernel: the column walk -- a workgroup owns 4 key blocks (32 keys per
 //    wavefront) grouped so that their columns nearly coincide (the strided global blocks
 //    together) and streams the Q and dO blocks, lse and D of the union of their columns;
-//    S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
-// Scores stay unscaled dot products of the bf16 inputs (exact products, fp32 sums); the row's
-// 8 * lse is subtracted before the one multiply by log2(e)/8 that feeds exp2.
+//    S = Q K'^T with K' = K * log2(e)/8 rounded to bf16 (the forward scales Q the same way),
+//    so that with lse * log2(e) and D folded into one MFMA step each P = exp2(S) takes no
+//    vector work before the exponential; then dV^T += dO^T P and dK^T += Q^T dS.
 // Every output row is written by exactly one wavefront, with no atomics: results are
 // deterministic.
 #include <type_traits>
@@ -44,9 +45,9 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kTileBytes = 64 * 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kScoreToLog2 = kLog2e / 8.0f;
-constexpr float kEmptyRowLse8 = 3.0e38f;
+constexpr float kEmptyRowLse2 = 3.0e38f;   // lse * log2(e) of a row with no key: p = 0
 // s_waitcnt operand: vmcnt <= 2 and lgkmcnt == 0, expcnt not waited for (gfx9 field layout)
-constexpr int kWaitVm2 = 2 | (7 << 4);      // 8 * lse of a row with no key: p = 0
+constexpr int kWaitVm2 = 2 | (7 << 4);
 static_assert(kBwdWaves == 8, "a 64 x 64 tile is 8 wave-loads of 1 KB, one per wavefront");
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile (the forward
@@ -77,11 +78,20 @@ __device__ __forceinline__ bf16x8 ones_slots(int g) {
   return g == 0 ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
 }
 
-// 8 channels (chunk c) of row `row` of a [rows, 64] bf16 tensor as an MFMA operand; zero
-// when !ok.
-__device__ __forceinline__ bf16x8 load_chunk(const uint16_t* base, int64_t row, int c, bool ok) {
+// 8 channels (chunk c) of row `row` of a [rows, 64] bf16 tensor as an MFMA operand,
+// optionally times log2(e)/8 (rounded to bf16); zero when !ok.
+__device__ __forceinline__ bf16x8 load_chunk(const uint16_t* base, int64_t row, int c, bool ok,
+                                             bool scale = false) {
   u32x4 raw{0u, 0u, 0u, 0u};
-  if (ok) raw = *reinterpret_cast<const u32x4*>(base + row * 64 + 8 * c);
+  if (ok) {
+    raw = *reinterpret_cast<const u32x4*>(base + row * 64 + 8 * c);
+    if (scale) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        raw[e] = pack_bf16x2(__uint_as_float(raw[e] << 16) * kScoreToLog2,
+                             __uint_as_float(raw[e] & 0xffff0000u) * kScoreToLog2);
+    }
+  }
   return __builtin_bit_cast(bf16x8, raw);
 }
 
@@ -136,9 +146,9 @@ __device__ __forceinline__ void copy_rows_f32(const float* slice, int32_t N, int
   __builtin_amdgcn_global_load_lds(slice + t, (lds_void*)dst, 4, 0, 0);
 }
 
-// D = rowsum(dO * O) and 8 * lse per row; one thread per 8-channel chunk of a row.
+// D = rowsum(dO * O) and lse * log2(e) per row; one thread per 8-channel chunk of a row.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* out, const uint16_t* dout, const float* lse,
-                                                       float* lse8, float* delta, int64_t rows) {
+                                                       float* lse2, float* delta, int64_t rows) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid >> 3;
   const int c = (int)(gid & 7);
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* out, cons
   if (c == 0) {
     delta[row] = s;
     const float l = lse[row];
-    lse8[row] = (l == -INFINITY) ? kEmptyRowLse8 : 8.0f * l;
+    lse2[row] = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
   }
 }
 
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   }
   // the row's lse (log2 units) enters each exponent through one FMA (it is the lane's own
   // constant); D is folded into the dP^T accumulator by one extra MFMA step
-  const float lse2 = (qok ? P.lse8[base + q] : kEmptyRowLse8) * kScoreToLog2;
+  const float lse2 = qok ? P.lse2[base + q] : kEmptyRowLse2;
   const float dlt = qok ? P.delta[base + q] : 0.f;
   const bf16x8 fold_d = fold_neg(dlt, g);
   const bf16x8 ones = ones_slots(g);
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   bf16x8 kf[4], vf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = load_chunk(P.k + base * 64, key, 2 * ks + g, kok);
+    kf[ks] = load_chunk(P.k + base * 64, key, 2 * ks + g, kok, true);
     vf[ks] = load_chunk(P.v + base * 64, key, 2 * ks + g, kok);
   }
   const bf16x8 ones = ones_slots(g);
@@ -430,7 +440,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   const int cnt = P.kg_cnt[grp];
   const uint16_t* qslice = P.q + base * 64;
   const uint16_t* oslice = P.dout + base * 64;
-  const float* lslice = P.lse8 + base;
+  const float* lslice = P.lse2 + base;
   const float* dslice = P.delta + base;
   auto copies = [&](int blk, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
     copy_tile(qslice, P.N, blk, qd, wave, lane);
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // S - 8 lse and dP - D for queries 32qt .. 32qt+31 (registers) and the wavefront's keys
+  // S' - lse * log2(e) (S' = Q K'^T, log2 units) and dP - D for queries 32qt .. 32qt+31 (registers) and the wavefront's keys
   // (lanes); the per-query lse and D enter through one folded MFMA step each
   auto sdp_half = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int qt,
                       f32x16& s, f32x16& dp) __attribute__((always_inline)) {
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     f32x16 p, ds;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(s[r] * kScoreToLog2);
+      p[r] = __builtin_amdgcn_exp2f(s[r]);
       ds[r] = p[r] * dp[r];
     }
     pack16(p, pb);
@@ -595,7 +605,7 @@ hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.bh_rows == 0) return hipSuccess;
   const int64_t threads = p.bh_rows * 8;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.out, p.dout,
-                     p.lse, p.lse8, p.delta, p.bh_rows);
+                     p.lse, p.lse2, p.delta, p.bh_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);

@@ -533,7 +533,7 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
   p.out = static_cast<const uint16_t*>(out);
   p.dout = static_cast<const uint16_t*>(dout);
   p.lse = lse;
-  p.lse8 = workspace;
+  p.lse2 = workspace;
   p.delta = workspace + bh * N;
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);

@@ -169,7 +169,7 @@ struct BwdParams {
   const uint16_t* out;      // forward output
   const uint16_t* dout;     // upstream gradient
   const float* lse;         // [BH, N] natural-log LSE of the forward
-  float* lse8;              // [BH, N] workspace: 8 * lse (3e38 for an empty row)
+  float* lse2;              // [BH, N] workspace: lse * log2(e) (3e38 for an empty row)
   float* delta;             // [BH, N] workspace: rowsum(dout * out)
   uint16_t* dq;
   uint16_t* dk;

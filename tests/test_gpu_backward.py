@@ -7,8 +7,10 @@ and on sampled keys of local-only key blocks (dk, dv), whose attending rows the 
 enumerate.
 
 Tolerance, from the arithmetic: P and dS enter the matrix cores rounded to bf16 (relative
-2^-9 each, independent across terms), D = rowsum(dO * O) uses the bf16 output O of the
-forward, and every gradient is rounded to bf16 once (2^-9 of its value).  Summed over
+2^-9 each, independent across terms), the key walk scores against K * log2(e)/8 rounded to
+bf16 (as the forward scores Q; a score error of ~2^-9 of each product), D = rowsum(dO * O)
+uses the bf16 output O of the forward, and every gradient is rounded to bf16 once (2^-9 of
+its value).  Summed over
 hundreds of terms with independent signs these stay near 2^-9 of the result in relative L2
 (<= 1e-2 asserted) and below 2^-6 of the compared set's largest magnitude element-wise
 (max-abs <= 2e-2 * max|ref| + 1e-6 asserted; at the workloads' sizes the gradients are
