@@ -110,6 +110,44 @@ def rmsnorm(x: np.ndarray, gamma, eps: float) -> np.ndarray:
     return x / np.sqrt(mean_sq + eps) * np.asarray(gamma, dtype=np.float64)
 
 
+def rope3d_transpose(x: np.ndarray, grid, theta: float = 10000.0, token_offset: int = 0) -> np.ndarray:
+    """The transpose (inverse) of rope3d: each channel pair rotated by minus its angle, which
+    maps the gradient of a rotated tensor to the gradient of its input."""
+    x = np.asarray(x, dtype=np.float64)
+    coords = token_coords(np.arange(np.shape(x)[-2]) + token_offset, grid)
+    out = x.copy()
+    for c0, width, axis in ROPE_SECTIONS:
+        pos = coords[axis].astype(np.float64)
+        for p in range(width // 2):
+            phi = pos * theta ** (-2.0 * p / width)
+            cos, sin = np.cos(phi), np.sin(phi)
+            a = x[..., c0 + 2 * p]
+            b = x[..., c0 + 2 * p + 1]
+            out[..., c0 + 2 * p] = a * cos + b * sin
+            out[..., c0 + 2 * p + 1] = b * cos - a * sin
+    return out
+
+
+def qk_norm_rope_backward(x: np.ndarray, gamma, eps: float, grid, dy: np.ndarray, theta: float = 10000.0,
+                          token_offset: int = 0):
+    """Gradients of sum(dy * qk_norm_rope(x)) with respect to x and gamma (grid None: the
+    RMSNorm alone), by the chain rule: dy_pre = R^T dy, n = x / r with
+    r = sqrt(mean(x^2) + eps), dgamma = sum over every row of dy_pre * n,
+    dn = dy_pre * gamma, dx = (dn - n * mean(dn * n)) / r.  Returns dx [..., N, 64] and
+    dgamma [64] (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    dy_pre = np.asarray(dy, dtype=np.float64)
+    if grid is not None:
+        dy_pre = rope3d_transpose(dy_pre, grid, theta, token_offset)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    n = x / r
+    dgamma = np.sum((dy_pre * n).reshape(-1, HEAD_DIM), axis=0)
+    dn = dy_pre * gamma
+    dx = (dn - n * np.mean(dn * n, axis=-1, keepdims=True)) / r
+    return dx, dgamma
+
+
 def qk_norm_rope(x: np.ndarray, gamma, eps: float, grid, theta: float = 10000.0, token_offset: int = 0) -> np.ndarray:
     """Query/key prologue of the self-attention: RMSNorm of each head's channels, then the
     partitioned 3D-RoPE of the token's position (norm first, rotation second, as the

@@ -505,6 +505,50 @@ def pin_backward_sampled_match_full(impl):
     assert np.array_equal(impl.token_mask(rows, keys, cond, local, stride), allowed[np.ix_(rows, keys)])
 
 
+# ------------------------------------------------------------------------ prologue backward
+def pin_rope_transpose(impl):
+    """R^T is the adjoint and the inverse of the rotation: <R x, y> = <x, R^T y> and
+    R^T R x = x, with a token offset."""
+    rng = np.random.default_rng(81)
+    grid = (3, 4, 5)
+    x = rng.standard_normal((2, 40, 64))
+    y = rng.standard_normal((2, 40, 64))
+    rx = impl.rope3d(x, grid, token_offset=13)
+    rty = impl.rope3d_transpose(y, grid, token_offset=13)
+    assert abs(float(np.sum(rx * y)) - float(np.sum(x * rty))) < 1e-10
+    assert np.max(np.abs(impl.rope3d_transpose(rx, grid, token_offset=13) - x)) < 1e-12
+
+
+def pin_prologue_backward_finite_differences(impl):
+    """dx and dgamma are the derivatives of L = sum(dy * qk_norm_rope(x)): central
+    differences (step 1e-6, fp64) on sampled coordinates of x and gamma, with the 3D-RoPE
+    (token offset 9) and without it (the RMSNorm alone), eps 1e-3 and 1e-6."""
+    rng = np.random.default_rng(82)
+    grid = (2, 3, 7)
+    x = rng.standard_normal((2, 30, 64)) * rng.uniform(0.1, 3.0, (2, 30, 1))
+    gamma = rng.uniform(0.5, 2.0, 64)
+    dy = rng.standard_normal((2, 30, 64))
+    h = 1e-6
+    for g, eps in ((grid, 1e-6), (None, 1e-3)):
+        def loss(xx, gg):
+            y = impl.rmsnorm(xx, gg, eps) if g is None else impl.qk_norm_rope(xx, gg, eps, g, token_offset=9)
+            return math.fsum((y * dy).ravel())
+        dx, dgamma = impl.qk_norm_rope_backward(x, gamma, eps, g, dy, token_offset=9)
+        for _ in range(12):
+            i, t, c = int(rng.integers(0, 2)), int(rng.integers(0, 30)), int(rng.integers(0, 64))
+            xp, xm = x.copy(), x.copy()
+            xp[i, t, c] += h
+            xm[i, t, c] -= h
+            num = (loss(xp, gamma) - loss(xm, gamma)) / (2 * h)
+            assert abs(num - dx[i, t, c]) < 1e-6 * max(1.0, abs(num)), (g, i, t, c, num, dx[i, t, c])
+        for c in rng.choice(64, 8, replace=False):
+            gp, gm = gamma.copy(), gamma.copy()
+            gp[c] += h
+            gm[c] -= h
+            num = (loss(x, gp) - loss(x, gm)) / (2 * h)
+            assert abs(num - dgamma[c]) < 1e-6 * max(1.0, abs(num)), (g, c, num, dgamma[c])
+
+
 # ------------------------------------------------------------------------- cross-attention
 def pin_cross_dense_sdpa(impl):
     """Without padding, cross-attention is plain softmax attention of the video queries over
@@ -607,5 +651,6 @@ ALL_PINS = [
     pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
     pin_backward_sampled_match_full, pin_cross_dense_sdpa, pin_cross_padding, pin_cross_brute_force,
-    pin_merge_of_key_partition, pin_merge_closed_form,
+    pin_merge_of_key_partition, pin_merge_closed_form, pin_rope_transpose,
+    pin_prologue_backward_finite_differences,
 ]

@@ -38,6 +38,11 @@ MUTANTS = {
                          "lse = np.where(empty, -np.inf, np.log(l_safe))")],
     "scores_use_v": [("s = (q @ k.T) * SOFTMAX_SCALE", "s = (q @ v.T) * SOFTMAX_SCALE")],
     "no_normalisation": [("out = (e @ v) / l_safe[:, None]", "out = (e @ v)")],
+    "rope_transpose_sign": [("out[..., c0 + 2 * p] = a * cos + b * sin", "out[..., c0 + 2 * p] = a * cos - b * sin")],
+    "prologue_bwd_no_projection": [("dx = (dn - n * np.mean(dn * n, axis=-1, keepdims=True)) / r", "dx = dn / r")],
+    "prologue_bwd_dgamma_before_rotation": [("dgamma = np.sum((dy_pre * n).reshape(-1, HEAD_DIM), axis=0)",
+                                             "dgamma = np.sum((np.asarray(dy) * n).reshape(-1, HEAD_DIM), axis=0)")],
+    "prologue_bwd_gain_dropped": [("dn = dy_pre * gamma", "dn = dy_pre")],
     "merge_weight_not_normalised": [("out += (wgt / total_safe)[..., None] * o", "out += wgt[..., None] * o")],
     "merge_lse_without_max": [("lse = np.where(empty, -np.inf, m_safe + np.log(total_safe))",
                                "lse = np.where(empty, -np.inf, np.log(total_safe))")],
