@@ -194,6 +194,33 @@ def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
             "what": "RMSNorm over each head's 64 channels with a 64-value gain, then 3D-RoPE, on Q and on K"}
 
 
+def measure_prologue_backward(bsa, torch, q, w, steps: int, stream) -> dict:
+    """Backward of the QK prologue on this workload's Q shape, HBM-bound: algorithmic bytes =
+    x and dy read, dx written (6 B per element); dgamma's partial sums are a few KB."""
+    gen = torch.Generator(device="cpu").manual_seed(16)
+    gq = (torch.rand(64, generator=gen) + 0.5).cuda()
+    dy = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
+    dx = torch.empty_like(q)
+    dg = torch.empty(64, dtype=torch.float32, device="cuda")
+    n_tokens = q.shape[-2]
+    n_outer = q.numel() // (64 * n_tokens)
+    ws = torch.empty(int(bsa.lib().lcv_qk_rmsnorm_rope3d_backward_workspace(n_outer, n_tokens)),
+                     dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        bsa.qk_rmsnorm_rope3d_backward(q, dy, gq, 1e-6, w.grid, dx=dx, dgamma=dg, workspace=ws)
+    ms = timed_launches(torch, stream,
+                        lambda: bsa.qk_rmsnorm_rope3d_backward(q, dy, gq, 1e-6, w.grid, dx=dx, dgamma=dg, workspace=ws),
+                        steps)
+    nbytes = 6.0 * q.numel()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] QK prologue backward: {ms:.4f} ms per tensor, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBS:.1f}% of HBM)")
+    del dy, dx, ws
+    return {"bound": "hbm", "kernel": "qk_prologue_bwd_kernel", "avg_launch_ms": round(ms, 4),
+            "bytes_per_launch": nbytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBS, 4), "launches": steps,
+            "what": "gradients dx and dgamma of RMSNorm + 3D-RoPE for one Q-shaped tensor"}
+
+
 def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: int, stream) -> dict:
     """The attention backward (dQ, dK, dV from the forward's output and LSE) on this
     workload, timed apart from the forward step (q and k taken as already rotated).
@@ -496,6 +523,8 @@ def main() -> int:
         result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
     if not args.no_backward and extras:
         result["backward"] = measure_backward(bsa, torch, q, k, v, layout, w, flops, args.steps, stream)
+        if not args.no_prologue:
+            result["qk_prologue_backward"] = measure_prologue_backward(bsa, torch, q, w, args.steps, stream)
     if not args.no_cross and extras:
         result["cross_attention"] = measure_cross(bsa, torch, q, w, args.steps, stream)
     if not args.no_merge and extras:

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 
 # Every symbol include/lcv_bsa.h declares.
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
-            "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d", "lcv_bsa_forward",
+            "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d",
+            "lcv_qk_rmsnorm_rope3d_backward_workspace", "lcv_qk_rmsnorm_rope3d_backward", "lcv_bsa_forward",
             "lcv_bsa_forward_cached", "lcv_bsa_forward_rows", "lcv_bsa_backward", "lcv_cross_attention", "lcv_attn_merge",
             "lcv_last_error", "lcv_abi_version")
 
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         "lcv_bsa_layout_destroy": (None, [vp]),
         "lcv_rope3d_apply": (i32, [vp, vp, i64, i32, i32, ctypes.POINTER(Rope3dGrid), vp]),
         "lcv_qk_rmsnorm_rope3d": (i32, [vp, vp, vp, ctypes.c_float, i64, i32, i32, ctypes.POINTER(Rope3dGrid), vp]),
+        "lcv_qk_rmsnorm_rope3d_backward_workspace": (i64, [i64, i32]),
+        "lcv_qk_rmsnorm_rope3d_backward": (i32, [vp, vp, vp, ctypes.c_float, i64, i32, i32, ctypes.POINTER(Rope3dGrid),
+                                                 vp, vp, vp, i64, vp]),
         "lcv_bsa_forward": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), vp, vp, vp]),
         "lcv_bsa_forward_cached": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid),
                                          vp, vp, vp]),
@@ -223,6 +227,32 @@ def qk_rmsnorm_rope3d(x, gamma, eps: float = 1e-6, grid=None, token_offset: int 
                                        n_tokens, token_offset, ctypes.byref(g.c()) if g is not None else None,
                                        _stream_ptr(stream)))
     return y
+
+
+def qk_rmsnorm_rope3d_backward(x, dy, gamma, eps: float = 1e-6, grid=None, token_offset: int = 0, dx=None,
+                               dgamma=None, workspace=None, stream=None):
+    """Gradients (dx, dgamma) of qk_rmsnorm_rope3d(x, gamma, eps, grid, token_offset) for the
+    upstream gradient dy (bf16, the shape of x); dx may be x or dy."""
+    import torch
+    g = _as_grid(grid)
+    if x.shape[-1] != 64 or dy.shape != x.shape:
+        raise ValueError("x and dy must share the shape [..., n_tokens, 64]")
+    if gamma.dtype != torch.float32 or not gamma.is_cuda or not gamma.is_contiguous() or gamma.numel() != 64:
+        raise ValueError("gamma must be a contiguous float32 CUDA tensor of 64 values")
+    n_tokens = x.shape[-2]
+    n_outer = x.numel() // (64 * n_tokens) if n_tokens else 0
+    dx = torch.empty_like(x) if dx is None else dx
+    if dx.shape != x.shape:
+        raise ValueError("dx must have the shape of x")
+    dgamma = torch.empty(64, dtype=torch.float32, device=x.device) if dgamma is None else dgamma
+    need = int(lib().lcv_qk_rmsnorm_rope3d_backward_workspace(n_outer, n_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.float32, device=x.device)
+    _check(lib().lcv_qk_rmsnorm_rope3d_backward(_bf16(x, "x"), _bf16(dy, "dy"), gamma.data_ptr(), float(eps), n_outer,
+                                                n_tokens, token_offset, ctypes.byref(g.c()) if g is not None else None,
+                                                _bf16(dx, "dx"), dgamma.data_ptr(), workspace.data_ptr(),
+                                                workspace.numel(), _stream_ptr(stream)))
+    return dx, dgamma
 
 
 def _flags(rope_q: bool, rope_k: bool) -> int:

@@ -13,7 +13,8 @@ LIB_NAME = "liblcv_bsa.so"
 LIB_PATH = PKG / LIB_NAME
 
 SOURCES = ["lcv_bsa_host.cpp", "layout_kernels.hip", "rope3d_kernel.hip", "qk_prologue_kernel.hip",
-           "bsa_fwd_kernel.hip", "bsa_bwd_kernel.hip", "attn_merge_kernel.hip"]
+           "bsa_fwd_kernel.hip", "bsa_bwd_kernel.hip", "attn_merge_kernel.hip",
+           "qk_prologue_bwd_kernel.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code; the host pass ignores the flag.
 HIPCC_FLAGS = [

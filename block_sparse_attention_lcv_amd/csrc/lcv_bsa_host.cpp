@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "lcv_internal.h"
+#include "prologue_bwd.h"
 
 struct lcv_bsa_layout {
   lcv_bsa_layout_info info;
@@ -428,6 +429,48 @@ lcv_status lcv_qk_rmsnorm_rope3d(const void* x, void* y, const float* gamma, flo
       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), gamma, eps, n_outer, n_tokens, token_offset,
       grid != nullptr, grid ? grid->H : 1, grid ? grid->W : 1, grid ? std::log2(grid->theta) : 0.f, stream);
   if (e != hipSuccess) return hip_fail(e, "qk prologue launch");
+  return ok();
+}
+
+int64_t lcv_qk_rmsnorm_rope3d_backward_workspace(int64_t n_outer, int32_t n_tokens) {
+  if (n_outer < 0 || n_tokens < 0) return -1;
+  return lcv::prologue_bwd_workspace_floats(n_outer, n_tokens);
+}
+
+lcv_status lcv_qk_rmsnorm_rope3d_backward(const void* x, const void* dy, const float* gamma, float eps,
+                                          int64_t n_outer, int32_t n_tokens, int32_t token_offset,
+                                          const lcv_rope3d_grid* grid, void* dx, float* dgamma, float* workspace,
+                                          int64_t workspace_floats, hipStream_t stream) {
+  if (x == nullptr || dy == nullptr || gamma == nullptr || dx == nullptr || dgamma == nullptr || workspace == nullptr)
+    return fail(LCV_ERR_NULL, "x, dy, gamma, dx, dgamma and workspace are required");
+  if (n_outer < 0 || n_tokens < 0 || token_offset < 0)
+    return fail(LCV_ERR_INVALID_ARG, "n_outer, n_tokens and token_offset must be >= 0");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(LCV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16))
+    return fail(LCV_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
+  if (!aligned(gamma, 16) || !aligned(dgamma, 4) || !aligned(workspace, 4))
+    return fail(LCV_ERR_INVALID_ARG, "gamma must be 16-byte aligned, dgamma and workspace 4-byte aligned");
+  if (grid != nullptr) {
+    lcv_status st = check_grid(grid);
+    if (st != LCV_OK) return st;
+    const int64_t total = (int64_t)grid->T * grid->H * grid->W;
+    if ((int64_t)token_offset + n_tokens > total)
+      return fail(LCV_ERR_SHAPE, "tokens [%d, %lld) exceed the grid's %lld tokens", token_offset,
+                  (long long)token_offset + n_tokens, (long long)total);
+  } else if ((int64_t)token_offset + n_tokens >= (int64_t(1) << 31)) {
+    return fail(LCV_ERR_UNSUPPORTED, "token_offset + n_tokens must be below 2^31");
+  }
+  if (n_outer > (int64_t)65535 * lcv::kPrologueBwdSlices)
+    return fail(LCV_ERR_UNSUPPORTED, "n_outer above %lld is not supported", (long long)65535 * lcv::kPrologueBwdSlices);
+  const int64_t need = lcv::prologue_bwd_workspace_floats(n_outer, n_tokens);
+  if (workspace_floats < need)
+    return fail(LCV_ERR_INVALID_ARG, "workspace holds %lld floats, %lld needed", (long long)workspace_floats,
+                (long long)need);
+  const hipError_t e = lcv::launch_qk_prologue_bwd(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), gamma, eps, n_outer, n_tokens, token_offset,
+      grid != nullptr, grid ? grid->H : 1, grid ? grid->W : 1, grid ? std::log2(grid->theta) : 0.f,
+      static_cast<uint16_t*>(dx), dgamma, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "qk prologue backward launch");
   return ok();
 }
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 6
+#define LCV_BSA_ABI_VERSION 7
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -193,6 +193,24 @@ lcv_status lcv_bsa_forward_rows(const void* q, const void* k, const void* v, int
                                 const lcv_bsa_layout* layout, int32_t cond_len, uint32_t flags,
                                 const lcv_rope3d_grid* grid, int32_t row_begin, int32_t row_end, void* out, float* lse,
                                 hipStream_t stream);
+
+/* Backward of lcv_qk_rmsnorm_rope3d for LoRA training of the projections before it (myzaker
+ * article, technical principles: RMSNorm and 3D RoPE in the self-attention; the LoRA-trained
+ * refinement expert): with n = x / sqrt(mean(x^2) + eps) and dy' = R^T dy (each channel pair
+ * rotated by minus its angle; dy' = dy when grid is NULL),
+ *   dgamma = sum over every row of dy' * n,  dx = (dn - n * mean(dn * n)) / sqrt(mean(x^2) + eps),
+ *   dn = dy' * gamma.
+ *   x, dy, dx : bf16 [n_outer, n_tokens, 64] (x the prologue's input; dx may be x or dy)
+ *   gamma     : fp32 [64], 16-byte aligned;  dgamma : fp32 [64], written (not accumulated)
+ *   workspace : fp32, caller-owned, at least lcv_qk_rmsnorm_rope3d_backward_workspace(n_outer,
+ *               n_tokens) values (one 64-value partial per workgroup)
+ * Deterministic (the partials are added in a fixed order).  Asynchronous on stream.  Errors:
+ * NULL, INVALID_ARG (sizes, alignment, eps, small workspace), SHAPE, UNSUPPORTED, HIP. */
+int64_t lcv_qk_rmsnorm_rope3d_backward_workspace(int64_t n_outer, int32_t n_tokens);
+lcv_status lcv_qk_rmsnorm_rope3d_backward(const void* x, const void* dy, const float* gamma, float eps,
+                                          int64_t n_outer, int32_t n_tokens, int32_t token_offset,
+                                          const lcv_rope3d_grid* grid, void* dx, float* dgamma, float* workspace,
+                                          int64_t workspace_floats, hipStream_t stream);
 
 /* Backward of lcv_bsa_forward (flags = 0): the gradients of the attention for the upstream
  * gradient dout, for training (myzaker article, technical principles: the LoRA-trained

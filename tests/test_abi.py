@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 6
+    assert bsa.lib().lcv_abi_version() == 7
 
 
 QUERY_CASES = [
@@ -135,6 +135,24 @@ def test_merge_argument_errors():
     assert f(bad, arr, 2, 10, p, None, None) == 2
     assert f(arr, arr, 2, 10, p, ctypes.c_void_p(4098), None) == 2
     assert f(arr, arr, 2, 0, p, None, None) == 0          # no rows: nothing to do
+
+
+def test_prologue_backward_argument_errors():
+    L = bsa.lib()
+    g = bsa.Rope3dGrid(2, 4, 8, 1e4)
+    p = ctypes.c_void_p(4096)
+    f = L.lcv_qk_rmsnorm_rope3d_backward
+    need = L.lcv_qk_rmsnorm_rope3d_backward_workspace(32, 86400)
+    assert need == 512 * 2 * 64                 # 512 token-group workgroups x 2 slice ranges
+    assert L.lcv_qk_rmsnorm_rope3d_backward_workspace(3, 64) == 2 * 64     # 64 tokens = 2 token groups
+    assert L.lcv_qk_rmsnorm_rope3d_backward_workspace(-1, 64) == -1
+    assert f(None, p, p, 1e-6, 1, 64, 0, ctypes.byref(g), p, p, p, 64, None) == 1
+    assert f(p, p, p, 1e-6, 1, 64, 0, ctypes.byref(g), p, p, None, 64, None) == 1
+    assert f(p, p, p, -1.0, 1, 64, 0, ctypes.byref(g), p, p, p, 64, None) == 2
+    assert f(p, p, ctypes.c_void_p(4100), 1e-6, 1, 64, 0, ctypes.byref(g), p, p, p, 64, None) == 2
+    assert f(p, p, p, 1e-6, 1, 64, 0, ctypes.byref(g), p, p, p, 127, None) == 2     # workspace too small
+    assert f(p, p, p, 1e-6, 1, 64, 1, ctypes.byref(g), p, p, p, 64, None) == 3      # 65 tokens > 64
+    assert f(p, p, p, 1e-6, 2000000, 64, 0, None, p, p, p, 1 << 40, None) == 6
 
 
 def test_backward_argument_errors():

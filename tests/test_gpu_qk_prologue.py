@@ -141,3 +141,84 @@ def test_feeds_attention(lib):
     ref, _ = oracle.bsa_forward(qn, kn, bf16_bits_to_f64(vb), grid, 0, 2, 4, rope_q=False, rope_k=False)
     assert_out_close(from_dev_f64(out), ref, "prologue + attention")
     layout.close()
+
+
+# ----------------------------------------------------------------------------- backward
+def _bwd_check(got_dx, got_dg, ref_dx, ref_dg, what):
+    """dx: fp32 math rounded once to bf16 (relative L2 <= 1e-2, max-abs <= 2e-2 * max|ref|);
+    dgamma: fp32 sums over many rows of exact bf16 products (relative error <= 1e-4 of the
+    largest entry)."""
+    from tests.gpu_util import out_errors
+    max_abs, rel = out_errors(got_dx, ref_dx)
+    scale = float(np.max(np.abs(ref_dx)))
+    say(f"  {what}: dx max_abs {max_abs:.3e} (max|ref| {scale:.3e}) rel_l2 {rel:.3e}; "
+        f"dgamma max err {float(np.max(np.abs(got_dg - ref_dg))):.3e} (max|ref| {float(np.max(np.abs(ref_dg))):.3e})")
+    assert np.all(np.isfinite(got_dx)) and np.all(np.isfinite(got_dg))
+    assert rel <= 1e-2 and max_abs <= 2e-2 * scale, (max_abs, rel)
+    assert np.max(np.abs(got_dg - ref_dg)) <= 1e-4 * float(np.max(np.abs(ref_dg))) + 1e-6
+
+
+@pytest.mark.parametrize("grid,heads,offset,n_tokens", [
+    ((4, 8, 16), 2, 0, None),
+    ((3, 10, 21), 3, 0, None),          # 630 tokens: partial token group
+    ((3, 10, 21), 2, 210, 420),         # token offset
+    ((2, 5, 7), 37, 0, None),           # 37 slices: 3 slice ranges, the last with 5 (odd) slices
+    (None, 2, 0, 333),                  # RMSNorm alone
+])
+def test_prologue_backward_parity(lib, grid, heads, offset, n_tokens):
+    import torch
+    from lcv_inputs import grad_bits
+    total = grid[0] * grid[1] * grid[2] if grid else n_tokens
+    n = total - offset if n_tokens is None else n_tokens
+    say(f"[qk-prologue bwd] grid={grid} heads={heads} offset={offset} n={n}")
+    x_bits, _, _ = qkv_bits(23, 1, heads, n)
+    dy_bits = grad_bits(23, 1, heads, n)
+    g = _gamma(9)
+    dx, dg = lib.qk_rmsnorm_rope3d_backward(to_dev(x_bits), to_dev(dy_bits), _dev_gamma(g), EPS, grid,
+                                            token_offset=offset)
+    torch.cuda.synchronize()
+    ref_dx, ref_dg = oracle.qk_norm_rope_backward(bf16_bits_to_f64(x_bits), g, EPS, grid, bf16_bits_to_f64(dy_bits),
+                                                  token_offset=offset)
+    _bwd_check(from_dev_f64(dx), dg.cpu().numpy().astype(np.float64), ref_dx, ref_dg, "parity")
+    # in place over dy gives the same bits; a second call the same dgamma bits
+    dy2 = to_dev(dy_bits)
+    _, dg2 = lib.qk_rmsnorm_rope3d_backward(to_dev(x_bits), dy2, _dev_gamma(g), EPS, grid, token_offset=offset,
+                                            dx=dy2)
+    torch.cuda.synchronize()
+    assert torch.equal(dy2.view(torch.int16), dx.view(torch.int16))
+    assert torch.equal(dg2, dg)
+
+
+def test_prologue_backward_workload(lib):
+    """Full [1, 32, N, 64] tensors of the 720p workload: dx on sampled tokens against the
+    oracle; dgamma against the oracle over all rows of 4 heads (the same kernel path)."""
+    import torch
+    from lcv_inputs import grad_bits
+    w = WORKLOADS["t2v720"]
+    say("[qk-prologue bwd] t2v720 full shape")
+    x_bits, _, _ = qkv_bits(w.seed, 1, w.heads, w.n_tokens)
+    dy_bits = grad_bits(w.seed, 1, w.heads, w.n_tokens)
+    g = _gamma(10)
+    dx, _ = lib.qk_rmsnorm_rope3d_backward(to_dev(x_bits), to_dev(dy_bits), _dev_gamma(g), EPS, w.grid)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dx.float()).all()
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([[0, 1, w.n_tokens - 1], rng.integers(0, w.n_tokens, 100)]))
+    got = from_dev_f64(dx[:, :, torch.from_numpy(toks).cuda()])
+    xs = bf16_bits_to_f64(x_bits[:, :, toks])
+    dys = bf16_bits_to_f64(dy_bits[:, :, toks])
+    # rows at arbitrary tokens: rotate back with the per-token positions
+    ref_dx = np.zeros_like(xs)
+    for i, t in enumerate(toks):
+        ref_dx[:, :, i:i + 1], _ = oracle.qk_norm_rope_backward(xs[:, :, i:i + 1], g, EPS, w.grid, dys[:, :, i:i + 1],
+                                                                token_offset=int(t))
+    from tests.gpu_util import out_errors
+    max_abs, rel = out_errors(got, ref_dx)
+    assert rel <= 1e-2 and max_abs <= 2e-2 * float(np.max(np.abs(ref_dx))), (max_abs, rel)
+    x4, dy4 = x_bits[:, :4], dy_bits[:, :4]
+    _, dg4 = lib.qk_rmsnorm_rope3d_backward(to_dev(x4), to_dev(dy4), _dev_gamma(g), EPS, w.grid)
+    torch.cuda.synchronize()
+    _, ref_dg = oracle.qk_norm_rope_backward(bf16_bits_to_f64(x4), g, EPS, w.grid, bf16_bits_to_f64(dy4))
+    got_dg = dg4.cpu().numpy().astype(np.float64)
+    say(f"  dgamma over 4 heads: max err {float(np.max(np.abs(got_dg - ref_dg))):.3e} of {float(np.max(np.abs(ref_dg))):.3e}")
+    assert np.max(np.abs(got_dg - ref_dg)) <= 1e-4 * float(np.max(np.abs(ref_dg)))
