@@ -368,6 +368,22 @@ def cross_attention(q, k, v, kv_lens=None, rows=None):
     return out, lse
 
 
+def cross_attention_backward(q, k, v, dout, kv_lens=None):
+    """Gradients dq [B, H, N, 64], dk and dv [B, H, L, 64] of cross_attention for the upstream
+    gradient dout, by the chain rule through the row softmax (padded text tokens, k >=
+    kv_lens[b], get zero gradients)."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    bsz, heads, n_q, _ = q.shape
+    n_kv = k.shape[2]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(bsz):
+        length = n_kv if kv_lens is None else int(kv_lens[b])
+        mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (n_q, n_kv))
+        for h in range(heads):
+            dq[b, h], dk[b, h], dv[b, h] = masked_attention_backward(q[b, h], k[b, h], v[b, h], mask, dout[b, h])
+    return dq, dk, dv
+
+
 def merge_partials(outs, lses):
     """Merge attention results over disjoint key sets: outs [P][..., R, 64], lses [P][..., R]
     (float64) -> out [..., R, 64], lse [..., R].  lse = log(sum_i exp(lse_i)) (taken around the

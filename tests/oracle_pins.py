@@ -642,6 +642,38 @@ def pin_merge_closed_form(impl):
     assert np.all(out == 0.0) and lse[0] == -np.inf
 
 
+def pin_cross_backward(impl):
+    """Cross-attention gradients are the derivatives of L = sum(dout * out): central
+    differences on sampled coordinates of q, k and v with a padded batch item; padded text
+    tokens get exactly zero gradients; without padding the key gradients of a head sum to zero
+    and the value gradients to the sum of dout."""
+    rng = np.random.default_rng(85)
+    q = rng.standard_normal((2, 1, 40, 64))
+    k = rng.standard_normal((2, 1, 20, 64))
+    v = rng.standard_normal((2, 1, 20, 64))
+    do = rng.standard_normal((2, 1, 40, 64))
+    lens = [20, 13]
+    dq, dk, dv = impl.cross_attention_backward(q, k, v, do, kv_lens=lens)
+
+    def loss(qq, kk, vv):
+        out, _ = impl.cross_attention(qq, kk, vv, kv_lens=lens)
+        return math.fsum((out * do).ravel())
+    h = 1e-5
+    for which, grad, shape in ((0, dq, q.shape), (1, dk, k.shape), (2, dv, v.shape)):
+        for _ in range(10):
+            b, t, c = int(rng.integers(0, 2)), int(rng.integers(0, shape[2])), int(rng.integers(0, 64))
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][b, 0, t, c] += h
+            lp = loss(*args)
+            args[which][b, 0, t, c] -= 2 * h
+            lm = loss(*args)
+            num = (lp - lm) / (2 * h)
+            assert abs(num - grad[b, 0, t, c]) < 1e-6 * max(1.0, abs(num)), (which, b, t, c, num, grad[b, 0, t, c])
+    assert np.all(dk[1, :, 13:] == 0.0) and np.all(dv[1, :, 13:] == 0.0)
+    assert np.max(np.abs(dk[0, 0].sum(axis=0))) < 1e-10
+    assert np.max(np.abs(dv[0, 0].sum(axis=0) - do[0, 0].sum(axis=0))) < 1e-10
+
+
 ALL_PINS = [
     pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
@@ -652,5 +684,5 @@ ALL_PINS = [
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
     pin_backward_sampled_match_full, pin_cross_dense_sdpa, pin_cross_padding, pin_cross_brute_force,
     pin_merge_of_key_partition, pin_merge_closed_form, pin_rope_transpose,
-    pin_prologue_backward_finite_differences,
+    pin_prologue_backward_finite_differences, pin_cross_backward,
 ]

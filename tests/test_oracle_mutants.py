@@ -43,6 +43,8 @@ MUTANTS = {
     "prologue_bwd_dgamma_before_rotation": [("dgamma = np.sum((dy_pre * n).reshape(-1, HEAD_DIM), axis=0)",
                                              "dgamma = np.sum((np.asarray(dy) * n).reshape(-1, HEAD_DIM), axis=0)")],
     "prologue_bwd_gain_dropped": [("dn = dy_pre * gamma", "dn = dy_pre")],
+    "cross_bwd_padding_ignored": [("        length = n_kv if kv_lens is None else int(kv_lens[b])\n        mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (n_q, n_kv))\n        for h in range(heads):\n            dq[b, h], dk[b, h], dv[b, h]",
+                                   "        length = n_kv\n        mask = np.broadcast_to(np.arange(n_kv)[None, :] < length, (n_q, n_kv))\n        for h in range(heads):\n            dq[b, h], dk[b, h], dv[b, h]")],
     "merge_weight_not_normalised": [("out += (wgt / total_safe)[..., None] * o", "out += wgt[..., None] * o")],
     "merge_lse_without_max": [("lse = np.where(empty, -np.inf, m_safe + np.log(total_safe))",
                                "lse = np.where(empty, -np.inf, np.log(total_safe))")],
