@@ -235,7 +235,7 @@ def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarr
     mask is empty give out = 0 and lse = -inf."""
     s = (q @ k.T) * SOFTMAX_SCALE
     s = np.where(mask, s, -np.inf)
-    m = s.max(axis=1)
+    m = s.max(axis=1, initial=-np.inf)   # no key at all is an empty mask too
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
     e = np.exp(s - m_safe[:, None])
@@ -254,7 +254,7 @@ def masked_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask:
     dQ = dS K / 8, dK = dS^T Q / 8.  Rows with an empty mask contribute nothing."""
     s = (q @ k.T) * SOFTMAX_SCALE
     s = np.where(mask, s, -np.inf)
-    m = s.max(axis=1)
+    m = s.max(axis=1, initial=-np.inf)   # no key at all is an empty mask too
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
     e = np.exp(s - m_safe[:, None])

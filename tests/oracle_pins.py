@@ -674,6 +674,25 @@ def pin_cross_backward(impl):
     assert np.max(np.abs(dv[0, 0].sum(axis=0) - do[0, 0].sum(axis=0))) < 1e-10
 
 
+
+def pin_cross_no_text(impl):
+    """Without any text token a query attends nothing: out = 0, lse = -inf and dq = 0, the
+    same as a batch item whose valid length is 0; with no query, dk = dv = 0."""
+    rng = np.random.default_rng(86)
+    q = rng.standard_normal((1, 2, 30, 64))
+    do = rng.standard_normal((1, 2, 30, 64))
+    none = np.zeros((1, 2, 0, 64))
+    out, lse = impl.cross_attention(q, none, none)
+    assert out.shape == q.shape and np.all(out == 0.0) and np.all(lse == -np.inf)
+    dq, dk, dv = impl.cross_attention_backward(q, none, none, do)
+    assert np.all(dq == 0.0) and dk.shape == (1, 2, 0, 64) and dv.shape == (1, 2, 0, 64)
+    k = rng.standard_normal((1, 2, 9, 64))
+    dq0, dk0, dv0 = impl.cross_attention_backward(q, k, k, do, kv_lens=[0])
+    assert np.all(dq0 == 0.0) and np.all(dk0 == 0.0) and np.all(dv0 == 0.0)
+    _, dk1, dv1 = impl.cross_attention_backward(np.zeros((1, 2, 0, 64)), k, k, np.zeros((1, 2, 0, 64)))
+    assert np.all(dk1 == 0.0) and np.all(dv1 == 0.0)
+
+
 ALL_PINS = [
     pin_rope_norm, pin_rope_origin_identity, pin_rope_sections_textbook, pin_rope_relative_position,
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
@@ -684,5 +703,5 @@ ALL_PINS = [
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
     pin_backward_sampled_match_full, pin_cross_dense_sdpa, pin_cross_padding, pin_cross_brute_force,
     pin_merge_of_key_partition, pin_merge_closed_form, pin_rope_transpose,
-    pin_prologue_backward_finite_differences, pin_cross_backward,
+    pin_prologue_backward_finite_differences, pin_cross_backward, pin_cross_no_text,
 ]
