@@ -249,9 +249,10 @@ def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: in
             "what": "dQ, dK, dV of the block-sparse attention (D = rowsum(dO*O) pass, query walk, key walk)"}
 
 
-def measure_cross(bsa, torch, q, w, steps: int, stream) -> dict:
-    """Cross-attention of this workload's video queries over 512 text tokens (32 heads), timed
-    apart from the self-attention step: algorithmic FLOPs = 4 * 64 * N * L * heads (dense)."""
+def measure_cross(bsa, torch, q, w, steps: int, stream, with_backward: bool = True):
+    """Cross-attention of this workload's video queries over 512 text tokens (32 heads), and
+    its backward, timed apart from the self-attention step: algorithmic FLOPs of the forward
+    = 4 * 64 * N * L * heads (dense).  Returns (forward, backward or None)."""
     from lcv_inputs import TEXT_LEN
     gen = torch.Generator(device="cpu").manual_seed(14)
     shape = (q.shape[0], q.shape[1], TEXT_LEN, 64)
@@ -267,12 +268,39 @@ def measure_cross(bsa, torch, q, w, steps: int, stream) -> dict:
     nbytes = 2.0 * (2 * q.numel() + 2 * k.numel()) + 4.0 * lse.numel()
     log(f"[bench] cross-attention ({TEXT_LEN} text tokens): {ms:.4f} ms, {tf:.1f} TFLOP/s "
         f"({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% of MFMA peak; {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s of Q, O, K, V, lse)")
-    del k, v, out, lse
-    return {"bound": "mfma", "kernel": "bsa_fwd_kernel<cross>", "ms": round(ms, 4), "text_tokens": TEXT_LEN,
-            "flops": flops, "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "min_bytes": nbytes,
-            "hbm_gbs_at_min_bytes": round(nbytes / (ms * 1e-3) / 1e9, 1), "launches": steps,
-            "what": "video queries over 512 padded text tokens, dense softmax attention"}
+    fwd = {"bound": "mfma", "kernel": "bsa_fwd_kernel<cross>", "ms": round(ms, 4), "text_tokens": TEXT_LEN,
+           "flops": flops, "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "min_bytes": nbytes,
+           "hbm_gbs_at_min_bytes": round(nbytes / (ms * 1e-3) / 1e9, 1), "launches": steps,
+           "what": "video queries over 512 padded text tokens, dense softmax attention"}
+    if not with_backward:
+        del k, v, out, lse
+        return fwd, None
+    # backward: effective rate by the usual convention, 2.5x the forward's FLOPs (S, dP, dV,
+    # dQ, dK); the kernels execute seven products (S and dP in both walks)
+    do = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(bsa.cross_attention_backward_workspace(q.shape[0], q.shape[1], q.shape[2], TEXT_LEN),
+                     dtype=torch.float32, device="cuda")
+
+    def call():
+        bsa.cross_attention_backward(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws)
+    for _ in range(3):
+        call()
+    bms = timed_launches(torch, stream, call, steps)
+    eff = 2.5 * flops / (bms * 1e-3) / 1e12
+    executed = 3.5 * flops / (bms * 1e-3) / 1e12
+    log(f"[bench] cross-attention backward: {bms:.4f} ms, {eff:.1f} TFLOP/s effective (2.5x forward FLOPs), "
+        f"{executed:.1f} TFLOP/s of executed matrix work")
+    del k, v, out, lse, do, dq, dk, dv, ws
+    bwd = {"bound": "mfma", "kernels": ["bwd_prep_kernel", "bwd_dq_kernel<cross>", "bwd_dkdv_kernel<cross>",
+                                        "bwd_cross_reduce_kernel"],
+           "ms": round(bms, 4), "effective_flops": 2.5 * flops, "achieved": round(eff, 3),
+           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / MFMA_BF16_PEAK_TFLOPS, 4),
+           "executed_tflops": round(executed, 3), "launches": steps,
+           "what": "dQ, dK, dV of the cross-attention over 512 text tokens (query chunks' fp32 partial dK, dV "
+                   "added in a fixed order)"}
+    return fwd, bwd
 
 
 def measure_merge(bsa, torch, q, steps: int, stream) -> dict:
@@ -526,7 +554,10 @@ def main() -> int:
         if not args.no_prologue:
             result["qk_prologue_backward"] = measure_prologue_backward(bsa, torch, q, w, args.steps, stream)
     if not args.no_cross and extras:
-        result["cross_attention"] = measure_cross(bsa, torch, q, w, args.steps, stream)
+        result["cross_attention"], cross_bwd = measure_cross(bsa, torch, q, w, args.steps, stream,
+                                                             with_backward=not args.no_backward)
+        if cross_bwd is not None:
+            result["cross_attention_backward"] = cross_bwd
     if not args.no_merge and extras:
         result["merge"] = measure_merge(bsa, torch, q, args.steps, stream)
     if args.copy_calibration:

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
             "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d",
             "lcv_qk_rmsnorm_rope3d_backward_workspace", "lcv_qk_rmsnorm_rope3d_backward", "lcv_bsa_forward",
-            "lcv_bsa_forward_cached", "lcv_bsa_forward_rows", "lcv_bsa_backward", "lcv_cross_attention", "lcv_attn_merge",
+            "lcv_bsa_forward_cached", "lcv_bsa_forward_rows", "lcv_bsa_backward", "lcv_cross_attention",
+            "lcv_cross_attention_backward_workspace", "lcv_cross_attention_backward", "lcv_attn_merge",
             "lcv_last_error", "lcv_abi_version")
 
 
@@ -85,6 +86,9 @@ def lib() -> ctypes.CDLL:
                                        vp]),
         "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp]),
         "lcv_cross_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "lcv_cross_attention_backward_workspace": (i64, [i32, i32, i32, i32]),
+        "lcv_cross_attention_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64,
+                                               vp]),
         "lcv_attn_merge": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, vp, vp, vp]),
         "lcv_last_error": (ctypes.c_char_p, []),
         "lcv_abi_version": (i32, []),
@@ -371,10 +375,61 @@ def cross_attention(q, k, v, kv_lens=None, out=None, lse=None, with_lse: bool = 
         raise ValueError("out must have the shape of q")
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
-    _check(lib().lcv_cross_attention(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), B, Hh, N, L,
-                                     None if kv_lens is None else kv_lens.data_ptr(), _bf16(out, "out"),
-                                     None if lse is None else lse.data_ptr(), _stream_ptr(stream)))
+    def ptr(t, name):   # tensors without rows may be empty (NULL)
+        p = _bf16(t, name)
+        return p if t.numel() else None
+
+    _check(lib().lcv_cross_attention(ptr(q, "q"), ptr(k, "k"), ptr(v, "v"), B, Hh, N, L,
+                                     None if kv_lens is None else kv_lens.data_ptr(), ptr(out, "out"),
+                                     None if lse is None or lse.numel() == 0 else lse.data_ptr(),
+                                     _stream_ptr(stream)))
     return out, lse
+
+
+def cross_attention_backward_workspace(batch: int, heads: int, n_q: int, kv_len: int) -> int:
+    """fp32 values of scratch that cross_attention_backward needs for these sizes."""
+    n = lib().lcv_cross_attention_backward_workspace(batch, heads, n_q, kv_len)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return n
+
+
+def cross_attention_backward(q, k, v, out, lse, dout, kv_lens=None, dq=None, dk=None, dv=None, workspace=None,
+                             stream=None):
+    """Gradients (dq, dk, dv) of cross_attention for the upstream gradient dout: q, out, dout
+    [B, H, N, 64], k, v [B, H, L, 64] (bf16), lse [B, H, N] (float32) from cross_attention."""
+    import torch
+    B, Hh, N, D = q.shape
+    if D != 64 or k.shape[:2] != (B, Hh) or k.shape[3] != 64 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, N, 64] and k, v [B, H, L, 64]")
+    L = k.shape[2]
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or lse.shape != (B, Hh, N):
+        raise ValueError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B
+                                or not kv_lens.is_contiguous()):
+        raise ValueError("kv_lens must be a contiguous int32 CUDA tensor of B values")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("dq must have the shape of q, dk and dv that of k")
+    need = cross_attention_backward_workspace(B, Hh, N, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 CUDA tensor")
+    def ptr(t, name):   # tensors of a side without rows may be empty (NULL)
+        p = _bf16(t, name)
+        return p if t.numel() else None
+
+    _check(lib().lcv_cross_attention_backward(
+        ptr(q, "q"), ptr(k, "k"), ptr(v, "v"), ptr(out, "out"), lse.data_ptr() if lse.numel() else None,
+        ptr(dout, "dout"), B, Hh, N, L, None if kv_lens is None else kv_lens.data_ptr(), ptr(dq, "dq"), ptr(dk, "dk"),
+        ptr(dv, "dv"), workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+    return dq, dk, dv
 
 
 def attn_merge(outs, lses, out=None, lse=None, with_lse: bool = True, stream=None):

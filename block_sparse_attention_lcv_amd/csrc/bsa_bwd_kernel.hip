@@ -22,6 +22,11 @@
 //    vector work before the exponential; then dV^T += dO^T P and dK^T += Q^T dS.
 // Every output row is written by exactly one wavefront, with no atomics: results are
 // deterministic.
+// Cross-attention (CROSS = true): keys and values are the text states [BH, kv_len, 64] with a
+// per-batch valid length; the query walk visits every text block, and since every query
+// block attends every text block the key walk splits the query blocks into chunks, each
+// workgroup writing fp32 partial dK, dV for its chunk, which bwd_cross_reduce_kernel adds in
+// chunk order (deterministic).
 #include <type_traits>
 
 #include "lcv_internal.h"
@@ -190,6 +195,19 @@ __device__ __forceinline__ int xcd_item() {
 }
 
 // ------------------------------------------------------------------------------------ dQ
+// Valid keys of a (batch, head) row: the sequence, or the batch item's text length.
+template <bool CROSS>
+__device__ __forceinline__ int key_end_of(const BwdParams& P, int bh) {
+  if constexpr (!CROSS) return P.N;
+  int len = P.kv_len;
+  if (P.kv_lens != nullptr) {
+    const int l = P.kv_lens[bh / P.heads];
+    len = l < 0 ? 0 : (l < P.kv_len ? l : P.kv_len);
+  }
+  return __builtin_amdgcn_readfirstlane(len);
+}
+
+template <bool CROSS>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams P) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
@@ -225,6 +243,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   const float lse2 = qok ? P.lse2[base + q] : kEmptyRowLse2;
   const float dlt = qok ? P.delta[base + q] : 0.f;
   const bf16x8 fold_d = fold_neg(dlt, g);
+  const int key_end = key_end_of<CROSS>(P, bh);                 // keys [0, key_end) exist
+  const int64_t kv_base = (int64_t)bh * (CROSS ? P.kv_len : P.N);
   const bf16x8 ones = ones_slots(g);
   uint32_t ka_off[4];
 #pragma unroll
@@ -237,20 +257,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
 
-  const const_i32* ents = (const const_i32*)(P.st_ent) + P.row_ptr[st * kWaves];
-  const int cnt = P.st_cnt[st];
-  const uint16_t* kslice = P.k + base * 64;
-  const uint16_t* vslice = P.v + base * 64;
+  // the workgroup's list: the forward's (self-attention), or every text block for all four
+  // query blocks (cross-attention)
+  const const_i32* ents = CROSS ? nullptr : (const const_i32*)(P.st_ent) + P.row_ptr[st * kWaves];
+  const int cnt = CROSS ? (key_end + 63) >> 6 : P.st_cnt[st];
+  auto entry = [&](int e) __attribute__((always_inline)) {
+    if constexpr (CROSS)
+      return (e << 8) | ((1 << kWaves) - 1);
+    else
+      return (int)ents[e];
+  };
+  const uint16_t* kslice = P.k + kv_base * 64;
+  const uint16_t* vslice = P.v + kv_base * 64;
   // three LDS stages: block e+2 is copied while block e is used and block e+1 lands
   int ent_cur = 0, ent_n1 = 0, ent_n2 = 0;
   if (cnt > 0) {
-    ent_cur = ents[0];
-    if (cnt > 1) ent_n1 = ents[1];
-    if (cnt > 2) ent_n2 = ents[2];
-    copy_tile(kslice, P.N, ent_cur >> 8, lds_k0, wave, lane);
-    copy_tile(vslice, P.N, ent_cur >> 8, lds_v0, wave, lane);
-    copy_tile(kslice, P.N, ent_n1 >> 8, lds_k1, wave, lane);
-    copy_tile(vslice, P.N, ent_n1 >> 8, lds_v1, wave, lane);
+    ent_cur = entry(0);
+    if (cnt > 1) ent_n1 = entry(1);
+    if (cnt > 2) ent_n2 = entry(2);
+    copy_tile(kslice, key_end, ent_cur >> 8, lds_k0, wave, lane);
+    copy_tile(vslice, key_end, ent_cur >> 8, lds_v0, wave, lane);
+    copy_tile(kslice, key_end, ent_n1 >> 8, lds_k1, wave, lane);
+    copy_tile(vslice, key_end, ent_n1 >> 8, lds_v1, wave, lane);
   }
   stage_barrier();
 
@@ -275,7 +303,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 64 * j + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool ok = key < P.N && (q >= P.C || key < P.C);
+      const bool ok = key < key_end && (q >= P.C || key < P.C);
       s[r] = ok ? s[r] : -INFINITY;
     }
   };
@@ -340,16 +368,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
     unsigned char* const vn = SN == 0 ? lds_v0 : SN == 1 ? lds_v1 : lds_v2;
     const int ent = ent_cur;
     const int jn = ent_n2 >> 8;
-    const int ent_after_raw = (e + 3 < cnt) ? ents[e + 3] : 0;
+    const int ent_after_raw = (e + 3 < cnt) ? entry(e + 3) : 0;
     // copies of block e+2 into the stage block e-1 used (past the end of the list they
     // re-read block 0, which nothing reads any more)
     auto copies = [&]() __attribute__((always_inline)) {
-      copy_tile(kslice, P.N, jn, kn, wave, lane);
-      copy_tile(vslice, P.N, jn, vn, wave, lane);
+      copy_tile(kslice, key_end, jn, kn, wave, lane);
+      copy_tile(vslice, key_end, jn, vn, wave, lane);
     };
     if (wave_on && ((ent >> (wave >> 1)) & 1)) {
       const int j = ent >> 8;
-      const bool masked = 64 * j + 63 >= P.N || (64 * qblk < P.C && 64 * j + 63 >= P.C);
+      const bool masked = 64 * j + 63 >= key_end || (64 * qblk < P.C && 64 * j + 63 >= P.C);
       if (masked)
         block(kc, vc, j, std::true_type{}, copies);
       else
@@ -389,6 +417,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
 }
 
 // ---------------------------------------------------------------------------------- dK, dV
+template <bool CROSS>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParams P) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_q0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_q1[kTileBytes];
@@ -407,19 +436,29 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   const int item = xcd_item();
   if (item >= P.bh * P.n_kg) return;
   const int bh = item / P.n_kg;
-  const int grp = item - bh * P.n_kg;
+  const int grp = item - bh * P.n_kg;           // self: a key group; cross: (group, chunk)
   const int64_t base = (int64_t)bh * P.N;
+  const int key_end = key_end_of<CROSS>(P, bh);
+  const int64_t kv_base = (int64_t)bh * (CROSS ? P.kv_len : P.N);
+  const int kgroup = CROSS ? grp / P.n_chunks : grp;
+  const int chunk = CROSS ? grp - kgroup * P.n_chunks : 0;
 
   // this wavefront's 32 keys; the lane's own key is key
-  const int kblk = __builtin_amdgcn_readfirstlane(P.kg_blk[grp * kWaves + (wave >> 1)]);
+  int kblk;
+  if constexpr (CROSS) {
+    kblk = kWaves * kgroup + (wave >> 1);
+    kblk = 64 * kblk < key_end ? kblk : -1;   // blocks past the text length: never read back
+  } else {
+    kblk = __builtin_amdgcn_readfirstlane(P.kg_blk[grp * kWaves + (wave >> 1)]);
+  }
   const bool wave_on = kblk >= 0;
   const int key = 64 * kblk + 32 * (wave & 1) + l32;
-  const bool kok = wave_on && key < P.N;
+  const bool kok = wave_on && key < (CROSS ? key_end : P.N);   // padded text rows stay zero
   bf16x8 kf[4], vf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = load_chunk(P.k + base * 64, key, 2 * ks + g, kok, true);
-    vf[ks] = load_chunk(P.v + base * 64, key, 2 * ks + g, kok);
+    kf[ks] = load_chunk(P.k + kv_base * 64, key, 2 * ks + g, kok, true);
+    vf[ks] = load_chunk(P.v + kv_base * 64, key, 2 * ks + g, kok);
   }
   const bf16x8 ones = ones_slots(g);
   uint32_t qa_off[4];
@@ -436,8 +475,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       dkt[dt][r] = 0.f;
     }
 
-  const int32_t* ents = P.kg_ent + P.kg_off[grp];
-  const int cnt = P.kg_cnt[grp];
+  // the workgroup's list: the host-built column union (self-attention), or the chunk's query
+  // blocks, all of which attend every text block (cross-attention)
+  const int32_t* ents = CROSS ? nullptr : P.kg_ent + P.kg_off[grp];
+  const int first_q = chunk * P.q_chunk;
+  int cnt;
+  if constexpr (CROSS) {
+    cnt = P.n_blocks - first_q;
+    cnt = cnt < P.q_chunk ? cnt : P.q_chunk;
+  } else {
+    cnt = P.kg_cnt[grp];
+  }
+  auto entry = [&](int e) __attribute__((always_inline)) {
+    if constexpr (CROSS)
+      return ((first_q + e) << 8) | ((1 << kWaves) - 1);
+    else
+      return ents[e];
+  };
   const uint16_t* qslice = P.q + base * 64;
   const uint16_t* oslice = P.dout + base * 64;
   const float* lslice = P.lse2 + base;
@@ -450,8 +504,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   };
   int ent_cur = 0, ent_next = 0;
   if (cnt > 0) {
-    ent_cur = __builtin_amdgcn_readfirstlane(ents[0]);
-    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(ents[1]);
+    ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
+    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
     copies(ent_cur >> 8, lds_q0, lds_o0, lds_l0, lds_d0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -481,7 +535,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qq = 64 * i + 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool ok = qq < P.N && (qq >= P.C || key < P.C);
+      const bool ok = qq < P.N && (CROSS ? key < key_end : (qq >= P.C || key < P.C));
       s[r] = ok ? s[r] : -INFINITY;
     }
   };
@@ -555,10 +609,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       else
         copies(in, lds_q1, lds_o1, lds_l1, lds_d1);
     };
-    const int ent_after_raw = (e + 2 < cnt) ? ents[e + 2] : 0;
+    const int ent_after_raw = (e + 2 < cnt) ? entry(e + 2) : 0;
     if (wave_on && ((ent >> (wave >> 1)) & 1)) {
       const int i = ent >> 8;
-      const bool masked = 64 * i + 63 >= P.N || (64 * i < P.C && 64 * kblk + 63 >= P.C);
+      const bool masked = CROSS ? (64 * i + 63 >= P.N || 64 * kblk + 63 >= key_end)
+                                : (64 * i + 63 >= P.N || (64 * i < P.C && 64 * kblk + 63 >= P.C));
       if (masked)
         block(qc, oc, lc, dc, i, std::true_type{}, next_copies);
       else
@@ -578,6 +633,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   }
   if (e < cnt) step(std::integral_constant<int, 0>{}, e);
 
+  if constexpr (CROSS) {
+    // fp32 partial sums of this chunk, dK already divided by 8: [chunk, BH, kv_len, 64]
+    if (kok) {
+      const int64_t prow = ((int64_t)chunk * P.bh + bh) * P.kv_len + key;
+      float* krow = P.part_dk + prow * 64;
+      float* vrow = P.part_dv + prow * 64;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          const float4 k4 = {dkt[dt][4 * R] * 0.125f, dkt[dt][4 * R + 1] * 0.125f, dkt[dt][4 * R + 2] * 0.125f,
+                             dkt[dt][4 * R + 3] * 0.125f};
+          const float4 v4 = {dvt[dt][4 * R], dvt[dt][4 * R + 1], dvt[dt][4 * R + 2], dvt[dt][4 * R + 3]};
+          *reinterpret_cast<float4*>(krow + 32 * dt + 8 * R + 4 * g) = k4;
+          *reinterpret_cast<float4*>(vrow + 32 * dt + 8 * R + 4 * g) = v4;
+        }
+    }
+    return;
+  }
   // dK = dK^T / 8, dV = dV^T; key rows written as 8-byte stores of 4 channels
   if (kok) {
     uint16_t* krow = P.dk + (base + key) * 64;
@@ -597,21 +671,85 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   }
 }
 
+// dK, dV of the cross-attention: the chunks' partial sums added in chunk order, rounded to
+// bf16; padded text rows (past the batch item's length) are zero.  One thread per 8 channels.
+__global__ __launch_bounds__(256) void bwd_cross_reduce_kernel(const BwdParams P) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 3;              // (bh, key)
+  const int c = (int)(gid & 7);
+  const int64_t rows = (int64_t)P.bh * P.kv_len;
+  if (row >= rows) return;
+  const int bh = (int)(row / P.kv_len);
+  const int key = (int)(row - (int64_t)bh * P.kv_len);
+  int len = P.kv_len;
+  if (P.kv_lens != nullptr) {
+    const int l = P.kv_lens[bh / P.heads];
+    len = l < 0 ? 0 : (l < P.kv_len ? l : P.kv_len);
+  }
+  float dk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (key < len) {
+    for (int ch = 0; ch < P.n_chunks; ++ch) {
+      const int64_t off = (((int64_t)ch * P.bh) * P.kv_len + row) * 64 + 8 * c;
+      const float4 k0 = *reinterpret_cast<const float4*>(P.part_dk + off);
+      const float4 k1 = *reinterpret_cast<const float4*>(P.part_dk + off + 4);
+      const float4 v0 = *reinterpret_cast<const float4*>(P.part_dv + off);
+      const float4 v1 = *reinterpret_cast<const float4*>(P.part_dv + off + 4);
+      dk[0] += k0.x; dk[1] += k0.y; dk[2] += k0.z; dk[3] += k0.w;
+      dk[4] += k1.x; dk[5] += k1.y; dk[6] += k1.z; dk[7] += k1.w;
+      dv[0] += v0.x; dv[1] += v0.y; dv[2] += v0.z; dv[3] += v0.w;
+      dv[4] += v1.x; dv[5] += v1.y; dv[6] += v1.z; dv[7] += v1.w;
+    }
+  }
+  u32x4 pk, pv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pk[e] = pack_bf16x2(dk[2 * e], dk[2 * e + 1]);
+    pv[e] = pack_bf16x2(dv[2 * e], dv[2 * e + 1]);
+  }
+  *reinterpret_cast<u32x4*>(P.dk + row * 64 + 8 * c) = pk;
+  *reinterpret_cast<u32x4*>(P.dv + row * 64 + 8 * c) = pv;
+}
+
 unsigned grid_for(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 
 }  // namespace
 
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
-  if (p.bh_rows == 0) return hipSuccess;
-  const int64_t threads = p.bh_rows * 8;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.out, p.dout,
-                     p.lse, p.lse2, p.delta, p.bh_rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid_for((int64_t)p.bh * p.n_kg)), dim3(kBwdThreads), 0, stream, p);
+  const bool cross = p.part_dk != nullptr;
+  hipError_t e = hipSuccess;
+  if (p.bh_rows > 0) {
+    const int64_t threads = p.bh_rows * 8;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.out, p.dout,
+                       p.lse, p.lse2, p.delta, p.bh_rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (!cross) {
+    return hipSuccess;
+  }
+  if (!cross) {   // self-attention
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(grid_for((int64_t)p.bh * p.n_kg)), dim3(kBwdThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+  }
+  // cross-attention; with no query (n_chunks = 0) the reduction writes dK = dV = 0
+  if (p.bh_rows > 0) {
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.n_kg > 0) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(grid_for((int64_t)p.bh * p.n_kg)), dim3(kBwdThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t reduce_threads = (int64_t)p.bh * p.kv_len * 8;
+  if (reduce_threads > 0)
+    hipLaunchKernelGGL(bwd_cross_reduce_kernel, dim3((unsigned)((reduce_threads + 255) / 256)), dim3(256), 0, stream,
+                       p);
   return hipGetLastError();
 }
 

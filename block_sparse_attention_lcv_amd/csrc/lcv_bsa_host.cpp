@@ -266,6 +266,39 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
   return ok();
 }
 
+// Work split of the cross-attention backward: the query walk takes four query blocks per
+// workgroup; the key walk takes four text blocks and one chunk of the query blocks, with
+// enough chunks to give the chip about 1024 workgroups; the chunks' fp32 partial dK, dV
+// follow lse2 and delta in the workspace (16-byte aligned).
+struct CrossBwdPlan {
+  int32_t n_q_blocks, n_kv_blocks, n_st, n_kg, n_chunks, q_chunk;
+  int64_t part_offset, part_floats, workspace_floats;
+};
+
+CrossBwdPlan cross_bwd_plan(int64_t bh, int32_t n_q, int32_t kv_len) {
+  CrossBwdPlan pl{};
+  pl.n_q_blocks = (int32_t)(((int64_t)n_q + 63) / 64);
+  pl.n_kv_blocks = (int32_t)(((int64_t)kv_len + 63) / 64);
+  pl.n_st = (pl.n_q_blocks + lcv::kWaves - 1) / lcv::kWaves;
+  const int64_t n_groups = (pl.n_kv_blocks + lcv::kWaves - 1) / lcv::kWaves;
+  int64_t chunks = 0;
+  if (pl.n_q_blocks > 0 && n_groups > 0) {
+    const int64_t per_chunk = bh * n_groups;
+    chunks = (1024 + per_chunk - 1) / per_chunk;
+    chunks = chunks < 64 ? chunks : 64;
+    chunks = chunks < pl.n_q_blocks ? chunks : pl.n_q_blocks;
+    pl.q_chunk = (int32_t)((pl.n_q_blocks + chunks - 1) / chunks);
+    chunks = (pl.n_q_blocks + pl.q_chunk - 1) / pl.q_chunk;   // no empty chunk
+  }
+  pl.n_chunks = (int32_t)chunks;
+  pl.n_kg = (int32_t)(n_groups * chunks);
+  const int64_t rows = bh * n_q;
+  pl.part_offset = (2 * rows + 3) / 4 * 4;
+  pl.part_floats = chunks * bh * kv_len * 64;
+  pl.workspace_floats = pl.part_offset + 2 * pl.part_floats;
+  return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -504,10 +537,11 @@ lcv_status lcv_attn_merge(const void* const* outs, const float* const* lses, int
 lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
                                int32_t n_q, int32_t kv_len, const int32_t* kv_lens, void* out, float* lse,
                                hipStream_t stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
-    return fail(LCV_ERR_NULL, "q, k, v and out are required");
   if (batch < 1 || heads < 1) return fail(LCV_ERR_INVALID_ARG, "batch and heads must be >= 1 (got %d, %d)", batch, heads);
   if (n_q < 0 || kv_len < 0) return fail(LCV_ERR_INVALID_ARG, "n_q and kv_len must be >= 0 (got %d, %d)", n_q, kv_len);
+  if (n_q > 0 && (q == nullptr || out == nullptr)) return fail(LCV_ERR_NULL, "q and out are required when n_q > 0");
+  if (n_q > 0 && kv_len > 0 && (k == nullptr || v == nullptr))
+    return fail(LCV_ERR_NULL, "k and v are required when n_q > 0 and kv_len > 0");
   for (const void* t : {q, k, v, static_cast<const void*>(out)})
     if (!aligned(t, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(LCV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
@@ -542,6 +576,73 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
   p.heads = heads;
   hipError_t e = lcv::launch_cross_fwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "cross-attention launch");
+  return ok();
+}
+
+int64_t lcv_cross_attention_backward_workspace(int32_t batch, int32_t heads, int32_t n_q, int32_t kv_len) {
+  if (batch < 1 || heads < 1 || n_q < 0 || kv_len < 0) return -1;
+  const CrossBwdPlan pl = cross_bwd_plan((int64_t)batch * heads, n_q, kv_len);
+  return pl.workspace_floats;
+}
+
+lcv_status lcv_cross_attention_backward(const void* q, const void* k, const void* v, const void* out,
+                                        const float* lse, const void* dout, int32_t batch, int32_t heads, int32_t n_q,
+                                        int32_t kv_len, const int32_t* kv_lens, void* dq, void* dk, void* dv,
+                                        float* workspace, int64_t workspace_floats, hipStream_t stream) {
+  if (batch < 1 || heads < 1) return fail(LCV_ERR_INVALID_ARG, "batch and heads must be >= 1 (got %d, %d)", batch, heads);
+  if (n_q < 0 || kv_len < 0) return fail(LCV_ERR_INVALID_ARG, "n_q and kv_len must be >= 0 (got %d, %d)", n_q, kv_len);
+  if (n_q > 0 && (q == nullptr || out == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
+    return fail(LCV_ERR_NULL, "q, out, lse, dout and dq are required when n_q > 0");
+  if (kv_len > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return fail(LCV_ERR_NULL, "k, v, dk and dv are required when kv_len > 0");
+  for (const void* t : {q, k, v, out, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (!aligned(t, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(workspace, 16))
+    return fail(LCV_ERR_INVALID_ARG, "lse must be 4-byte and workspace 16-byte aligned");
+  if (kv_lens != nullptr && !aligned(kv_lens, 4)) return fail(LCV_ERR_INVALID_ARG, "kv_lens must be 4-byte aligned");
+  const int64_t bh = (int64_t)batch * heads;
+  const CrossBwdPlan pl = cross_bwd_plan(bh, n_q, kv_len);
+  if (pl.workspace_floats > 0 && workspace == nullptr) return fail(LCV_ERR_NULL, "workspace is required");
+  if (workspace_floats < pl.workspace_floats)
+    return fail(LCV_ERR_INVALID_ARG, "workspace holds %lld values, %lld are needed", (long long)workspace_floats,
+                (long long)pl.workspace_floats);
+  const int64_t items = bh * (pl.n_st > pl.n_kg ? pl.n_st : pl.n_kg);
+  if (bh >= (int64_t(1) << 31) || items >= (int64_t(1) << 31) - 8 || bh * n_q * 8 >= (int64_t(1) << 40) ||
+      bh * kv_len * 8 >= (int64_t(1) << 40))
+    return fail(LCV_ERR_UNSUPPORTED, "batch * heads = %lld is too large", (long long)bh);
+  if (n_q == 0 && kv_len == 0) return ok();
+  hipError_t e;
+  lcv::BwdParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.lse2 = workspace;
+  p.delta = workspace + bh * n_q;
+  p.part_dk = workspace + pl.part_offset;
+  p.part_dv = p.part_dk + pl.part_floats;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.bh_rows = bh * n_q;
+  p.N = n_q;
+  p.C = 0;
+  p.n_blocks = pl.n_q_blocks;
+  p.n_st = pl.n_st;
+  p.n_kg = pl.n_kg;
+  p.bh = (int32_t)bh;
+  p.kv_len = kv_len;
+  p.kv_lens = kv_lens;
+  p.heads = heads;
+  p.n_kv_blocks = pl.n_kv_blocks;
+  p.q_chunk = pl.q_chunk;
+  p.n_chunks = pl.n_chunks;
+  e = lcv::launch_bsa_bwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "cross-attention backward launch");
   return ok();
 }
 

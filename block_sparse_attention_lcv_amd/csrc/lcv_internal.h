@@ -183,6 +183,15 @@ struct BwdParams {
   const int32_t* kg_ent;
   int64_t bh_rows;          // BH * N
   int32_t N, C, n_blocks, n_st, n_kg, bh;
+  // cross-attention (text keys/values [BH, kv_len, 64]); part_dk != nullptr selects it
+  int32_t kv_len;           // rows per (batch, head) of k and v
+  const int32_t* kv_lens;   // [B] valid text tokens, or nullptr
+  int32_t heads;
+  int32_t n_kv_blocks;      // ceil(kv_len / 64)
+  int32_t q_chunk;          // query blocks per key-walk workgroup
+  int32_t n_chunks;         // key-walk chunks of the query blocks
+  float* part_dk;           // [n_chunks, BH, kv_len, 64] fp32 partial sums
+  float* part_dv;
 };
 
 hipError_t launch_layout_build(const LayoutRule& L, const LayoutDev& d, hipStream_t stream);

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 7
+#define LCV_BSA_ABI_VERSION 8
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -241,12 +241,38 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
  *   kv_lens  : device int32 [batch] valid text tokens per batch item (keys at or past it are
  *              padding and ignored; values are clamped to [0, kv_len]), or NULL for kv_len
  *   lse      : fp32 [batch, heads, n_q] natural-log LSE of the scaled scores, or NULL
- * A batch item with no valid text token gives out = 0 and lse = -inf.  Caller-owned memory,
+ * A batch item with no valid text token gives out = 0 and lse = -inf.  With n_q = 0 every
+ * pointer, with kv_len = 0 k and v may be NULL.  Caller-owned memory,
  * no allocation, asynchronous on stream, deterministic.  Errors: NULL, INVALID_ARG (sizes,
  * alignment), UNSUPPORTED (sizes), HIP. */
 lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t heads,
                                int32_t n_q, int32_t kv_len, const int32_t* kv_lens, void* out, float* lse,
                                hipStream_t stream);
+
+/* Backward of lcv_cross_attention, for training the projections around it (myzaker article,
+ * technical principles: each block has 3D self-attention, cross-attention and a SwiGLU
+ * feed-forward network; the LoRA-trained refinement expert).  With P recomputed from the
+ * saved LSE over the valid text keys: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ * dQ = dS K / 8, dK = dS^T Q / 8.
+ *   q, out, dout : bf16 [batch, heads, n_q, 64];  lse : fp32 [batch, heads, n_q], the forward's
+ *   k, v         : bf16 [batch, heads, kv_len, 64];  kv_lens as in lcv_cross_attention
+ *   dq           : bf16 [batch, heads, n_q, 64];  dk, dv : bf16 [batch, heads, kv_len, 64];
+ *                  all written completely (padded text rows and a batch item without text
+ *                  get zeros)
+ *   workspace    : fp32, caller-owned, 16-byte aligned, at least
+ *                  lcv_cross_attention_backward_workspace(batch, heads, n_q, kv_len) values
+ *                  (per-row terms and the fp32 partial dK, dV of the query chunks; -1 for
+ *                  invalid sizes)
+ * With n_q = 0 (dk = dv = 0) the query-side pointers, with kv_len = 0 (dq = 0) the text-side
+ * pointers, and a workspace of size 0 may be NULL.
+ * Deterministic: the chunks' partial sums are added in a fixed order, without atomics.
+ * Asynchronous on stream.  Errors: NULL, INVALID_ARG (sizes, alignment, small workspace),
+ * UNSUPPORTED (sizes), HIP. */
+int64_t lcv_cross_attention_backward_workspace(int32_t batch, int32_t heads, int32_t n_q, int32_t kv_len);
+lcv_status lcv_cross_attention_backward(const void* q, const void* k, const void* v, const void* out,
+                                        const float* lse, const void* dout, int32_t batch, int32_t heads, int32_t n_q,
+                                        int32_t kv_len, const int32_t* kv_lens, void* dq, void* dk, void* dv,
+                                        float* workspace, int64_t workspace_floats, hipStream_t stream);
 
 /* Merge of attention results over disjoint key sets, the combine step of context-parallel
  * ring attention (myzaker article, technical principles: context-parallel ring block-sparse

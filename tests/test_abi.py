@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 7
+    assert bsa.lib().lcv_abi_version() == 8
 
 
 QUERY_CASES = [
@@ -109,6 +109,8 @@ def test_cross_attention_argument_errors():
     f = L.lcv_cross_attention
     assert f(None, p, p, 1, 1, 64, 64, None, p, None, None) == 1
     assert f(p, p, p, 1, 1, 64, 64, None, None, None, None) == 1
+    assert f(p, None, p, 1, 1, 64, 64, None, p, None, None) == 1
+    assert f(None, None, None, 1, 1, 0, 64, None, None, None, None) == 0   # no query: nothing read
     assert f(p, p, p, 0, 1, 64, 64, None, p, None, None) == 2
     assert f(p, p, p, 1, 1, -1, 64, None, p, None, None) == 2
     assert f(p, p, p, 1, 1, 64, -5, None, p, None, None) == 2
@@ -117,6 +119,58 @@ def test_cross_attention_argument_errors():
     assert f(p, p, p, 1, 1, 64, 64, ctypes.c_void_p(4097), p, None, None) == 2
     assert f(p, p, p, 1, 1, 0, 64, None, p, None, None) == 0          # no query: nothing to do
     assert f(p, p, p, 65536, 65536, 64, 64, None, p, None, None) == 6
+
+
+def _cross_bwd_workspace(batch, heads, n_q, kv_len):
+    """Expected scratch size: 2 values per query row (rounded up to 4), then fp32 partial dK
+    and dV per query chunk; chunks give about 1024 key-walk workgroups, at most 64 and at most
+    one per query block, none empty."""
+    bh = batch * heads
+    nqb, nkb = -(-n_q // 64), -(-kv_len // 64)
+    groups = -(-nkb // 4)
+    chunks = 0
+    if nqb and groups:
+        chunks = min(-(-1024 // (bh * groups)), 64, nqb)
+        per = -(-nqb // chunks)
+        chunks = -(-nqb // per)
+    return -(-2 * bh * n_q // 4) * 4 + 2 * chunks * bh * kv_len * 64
+
+
+def test_cross_backward_workspace_sizes():
+    f = bsa.lib().lcv_cross_attention_backward_workspace
+    for args in [(1, 1, 64, 64), (2, 3, 1000, 77), (1, 32, 58560, 512), (4, 2, 0, 512), (1, 1, 100, 0),
+                 (3, 5, 4097, 300)]:
+        assert f(*args) == _cross_bwd_workspace(*args), args
+    assert f(1, 1, 64, 64) == 128 + 2 * 64 * 64
+    assert f(0, 1, 64, 64) == -1 and f(1, 1, -1, 64) == -1 and f(1, 1, 64, -1) == -1
+
+
+def test_cross_backward_argument_errors():
+    L = bsa.lib()
+    p = ctypes.c_void_p(4096)
+    f = L.lcv_cross_attention_backward
+    big = 1 << 40
+
+    def call(q=p, lse=p, batch=1, heads=1, n_q=64, kv_len=64, kv_lens=None, ws=p, ws_n=big, dk=p):
+        return f(q, p, p, p, lse, p, batch, heads, n_q, kv_len, kv_lens, p, dk, p, ws, ws_n, None)
+
+    assert call(q=None) == 1
+    assert call(lse=None) == 1
+    assert call(ws=None) == 1
+    assert call(dk=None) == 1
+    assert call(q=None, lse=None, n_q=0, dk=None) == 1           # text side still needs dk
+    assert call(q=None, lse=None, n_q=0, kv_len=0, dk=None, ws=None, ws_n=0) == 0
+    assert call(batch=0) == 2
+    assert call(n_q=-1) == 2
+    assert call(kv_len=-3) == 2
+    assert call(q=ctypes.c_void_p(4104)) == 2
+    assert call(lse=ctypes.c_void_p(4098)) == 2
+    assert call(ws=ctypes.c_void_p(4100)) == 2                  # workspace needs 16-byte alignment
+    assert call(kv_lens=ctypes.c_void_p(4097)) == 2
+    assert call(ws_n=L.lcv_cross_attention_backward_workspace(1, 1, 64, 64) - 1) == 2
+    assert b"workspace" in L.lcv_last_error()
+    assert call(n_q=0, kv_len=0) == 0                            # nothing to compute
+    assert call(batch=65536, heads=65536, ws_n=1 << 62) == 6
 
 
 def test_merge_argument_errors():
