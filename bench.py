@@ -142,8 +142,58 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
         rows_n *= 2
     n_rows, dt, flops = best
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{w.name}: 1 of {w.heads} heads, {n_rows} random query rows of {w.n_tokens} "
+            "cpu": cpu_model(), "sample": f"{w.name}: 1 of {w.heads} heads, {n_rows} random query rows of {w.n_tokens} "
                       f"(fp64 numpy oracle: RoPE + masked dense attention), {dt:.2f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_blocks(w, seconds: float = 10.0) -> dict:
+    """The oracle's block-visiting form (each query block attends only the key blocks its CSR
+    row lists, fp64) on a bounded sample: one head, as many random query blocks as fit the
+    time budget (doubling from 4), scaled to effective attended TFLOP/s: the like-for-like
+    CPU analogue of a block-sparse CPU implementation."""
+    import oracle
+    from lcv_inputs import qkv_bits
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    qb, kb, vb = qkv_bits(w.seed, 1, 1, w.n_tokens)
+    q, k, v = bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+    n_blocks = -(-w.n_tokens // 64)
+    rng = np.random.default_rng(1)
+    count = 4
+    t_total = 0.0
+    while True:
+        blocks = rng.choice(n_blocks, size=min(count, n_blocks), replace=False)
+        t0 = time.perf_counter()
+        oracle.bsa_forward_blocks(q, k, v, w.grid, w.cond_len, w.local_blocks, w.global_stride, w.theta,
+                                  q_blocks=blocks)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        rows = np.concatenate([np.arange(64 * i, min(64 * i + 64, w.n_tokens)) for i in blocks])
+        flops = 4.0 * 64 * float(oracle.token_mask_rows(rows, w.n_tokens, w.cond_len, w.local_blocks,
+                                                        w.global_stride).sum())
+        best = (blocks.size, dt, flops)
+        if t_total >= seconds or count >= n_blocks or dt * 2 + t_total > 3 * seconds:
+            break
+        count *= 2
+    n_b, dt, flops = best
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle-block-visiting",
+            "cpu": cpu_model(),
+            "sample": f"{w.name}: 1 of {w.heads} heads, {n_b} random query blocks of {n_blocks} (fp64 numpy "
+                      f"oracle visiting only the CSR's key blocks: RoPE + attention), {dt:.2f} s"}
 
 
 def timed_launches(torch, stream, launch, count: int) -> float:
@@ -572,6 +622,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log("[bench] timing the oracle's block-visiting form on the host")
+        result["cpu_baseline_block_visiting"] = cpu_baseline_blocks(w, args.cpu_seconds / 2)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -24,7 +24,8 @@ fusion or reordering beyond what that definition states:
   keys (k < C)  [myzaker article, section on technical principles: block attention
   with a KV cache keeps condition tokens unaffected by noise tokens];
 * softmax attention with scale 1/sqrt(64) and the natural-log LSE of the scaled scores;
-* the CSR of attended key blocks per query block;
+* the CSR of attended key blocks per query block, and the attention evaluated block by
+  block over only the key blocks the CSR lists (the CPU block-sparse form);
 * the query/key prologue: RMSNorm over each head's 64 channels with a per-channel gain,
   then the 3D-RoPE  [myzaker article, section on technical principles: RMSNorm in the
   self-attention module, 3D RoPE on visual tokens];
@@ -343,6 +344,46 @@ def bsa_forward(q, k, v, grid, cond_len: int, local: int, stride: int, theta: fl
             if rope_k:
                 kb = rope3d(kb, grid, theta)
             out[b, h], lse[b, h] = masked_attention(qb, kb, v[b, h], mask)
+    return out, lse
+
+
+def bsa_forward_blocks(q, k, v, grid, cond_len: int, local: int, stride: int, theta: float = 10000.0,
+                       q_blocks=None):
+    """The same attention as bsa_forward, visiting only the attended key blocks: for each
+    query block i, the keys of the blocks that csr lists in row i are gathered and the block's
+    query rows attend them under the token mask (the condition rule and k < N).  A CPU
+    block-sparse implementation as the pages' Rust one is  [longcat-video-rs page, section
+    02 benchmark table: block-sparse self-attention with block=64, local=2, stride=4 on the
+    CPU], and the like-for-like CPU figure beside the GPU kernel.
+
+    q_blocks: optional query block indices to evaluate (all if None).
+    Returns out [B, H, R, 64] and lse [B, H, R] for the rows of those blocks, in order."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    bsz, heads, n_tokens, _ = q.shape
+    n = n_blocks_of(n_tokens)
+    q_blocks = np.arange(n) if q_blocks is None else np.asarray(q_blocks, dtype=np.int64)
+    row_ptr, col_idx = csr(n_tokens, cond_len, local, stride)
+    row_sets = [np.arange(i * BLOCK, min(i * BLOCK + BLOCK, n_tokens)) for i in q_blocks]
+    key_sets = []
+    for i in q_blocks:
+        cols = col_idx[row_ptr[i]:row_ptr[i + 1]]
+        key_sets.append(np.concatenate([np.arange(j * BLOCK, min(j * BLOCK + BLOCK, n_tokens)) for j in cols]))
+    n_rows = sum(r.size for r in row_sets)
+    out = np.zeros((bsz, heads, n_rows, HEAD_DIM))
+    lse = np.zeros((bsz, heads, n_rows))
+    for b in range(bsz):
+        for h in range(heads):
+            k_rot = rope3d(k[b, h], grid, theta)
+            at = 0
+            for rows, keys in zip(row_sets, key_sets):
+                q_rot = rope3d_at(q[b, h, rows], rows, grid, theta)
+                mask = token_mask(rows, keys, cond_len, local, stride)
+                o, l = masked_attention(q_rot, k_rot[keys], v[b, h, keys], mask)
+                out[b, h, at:at + rows.size] = o
+                lse[b, h, at:at + rows.size] = l
+                at += rows.size
     return out, lse
 
 

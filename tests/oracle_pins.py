@@ -414,6 +414,39 @@ def pin_sampled_rows_match_full(impl):
     assert np.max(np.abs(lse[:, :, rows] - lse_r)) < 1e-13
 
 
+def pin_block_visiting_equals_masked_dense(impl):
+    """Visiting only the attended key blocks gives the masked dense attention (to fp64
+    rounding): with the condition boundary inside a block and a ragged last block, for every
+    block and for an unordered subset; with no window and no global blocks it is dense
+    softmax attention inside each block (written out with a textbook row softmax here)."""
+    rng = np.random.default_rng(27)
+    grid = (2, 15, 21)
+    n = 630
+    q, k, v = (rng.standard_normal((1, 2, n, 64)) for _ in range(3))
+    out, lse = impl.bsa_forward(q, k, v, grid, 210, 2, 4)
+    out_b, lse_b = impl.bsa_forward_blocks(q, k, v, grid, 210, 2, 4)
+    assert np.max(np.abs(out - out_b)) < 1e-12 and np.max(np.abs(lse - lse_b)) < 1e-12
+    blocks = [9, 0, 3]
+    rows = np.concatenate([np.arange(64 * i, min(64 * i + 64, n)) for i in blocks])
+    out_s, lse_s = impl.bsa_forward_blocks(q, k, v, grid, 210, 1, 3, q_blocks=blocks)
+    out_r, lse_r = impl.bsa_forward(q, k, v, grid, 210, 1, 3, rows=rows)
+    assert np.max(np.abs(out_s - out_r)) < 1e-12 and np.max(np.abs(lse_s - lse_r)) < 1e-12
+    # no window, no global blocks, no condition: each block attends itself densely
+    out_d, lse_d = impl.bsa_forward_blocks(q, k, v, grid, 0, 0, 0, q_blocks=[4, 9])
+    qr = impl.rope3d(q[0, 0], grid)
+    kr = impl.rope3d(k[0, 0], grid)
+    at = 0
+    for i in (4, 9):
+        r = np.arange(64 * i, min(64 * i + 64, n))
+        sc = qr[r] @ kr[r].T / 8.0
+        mx = sc.max(axis=1, keepdims=True)
+        w = np.exp(sc - mx)
+        ref = (w / w.sum(axis=1, keepdims=True)) @ v[0, 0, r]
+        assert np.max(np.abs(out_d[0, 0, at:at + r.size] - ref)) < 1e-12
+        assert np.max(np.abs(lse_d[0, 0, at:at + r.size] - (mx[:, 0] + np.log(w.sum(axis=1))))) < 1e-12
+        at += r.size
+
+
 def pin_empty_row(impl):
     """A row with no attended key gives out = 0 and lse = -inf."""
     q = np.ones((2, 64))
@@ -698,7 +731,7 @@ ALL_PINS = [
     pin_rope_closed_form_first_pair, pin_token_mask_brute_force, pin_tiny_csr_golden,
     pin_two_block_layouts, pin_nnz_closed_form, pin_attended_pairs_closed_form,
     pin_two_block_brute_force, pin_full_layout_is_dense_sdpa, pin_condition_isolation,
-    pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_empty_row,
+    pin_cached_equals_full, pin_rope_shift_invariance, pin_sampled_rows_match_full, pin_block_visiting_equals_masked_dense, pin_empty_row,
     pin_rmsnorm_unit_rms, pin_rmsnorm_scale_invariance, pin_rmsnorm_closed_form, pin_qk_prologue_textbook,
     pin_qk_prologue_norm, pin_backward_finite_differences, pin_backward_sums, pin_backward_uniform_closed_form,
     pin_backward_sampled_match_full, pin_cross_dense_sdpa, pin_cross_padding, pin_cross_brute_force,

@@ -15,3 +15,16 @@ def test_attended_pairs_from(n, c, local, stride):
         ref = int(oracle.token_mask_rows(rows, n, c, local, stride).sum())
         assert bench.attended_pairs_from(n, c, local, stride, q_from) == ref
     assert bench.attended_pairs_from(n, c, local, stride, 0) == oracle.attended_pairs(n, c, local, stride)
+
+
+def test_cpu_baselines_report_their_sample():
+    """Both CPU figures of the benchmark run on the small workload and describe what they
+    timed (the block-visiting form over whole query blocks)."""
+    from lcv_inputs import WORKLOADS
+    w = WORKLOADS["tiny"]
+    dense = bench.cpu_baseline(w, 0.05)
+    blocks = bench.cpu_baseline_blocks(w, 0.05)
+    for r, kind in ((dense, "oracle"), (blocks, "oracle-block-visiting")):
+        assert r["kind"] == kind and r["unit"] == "TFLOP/s" and r["value"] > 0 and r["cores"] >= 1
+        assert w.name in r["sample"]
+    assert "query blocks" in blocks["sample"]

@@ -74,6 +74,11 @@ MUTANTS = {
                              "return rmsnorm(rope3d(x, grid, theta, token_offset), gamma, eps)")],
     "prologue_no_offset": [("return rope3d(rmsnorm(x, gamma, eps), grid, theta, token_offset)",
                             "return rope3d(rmsnorm(x, gamma, eps), grid, theta, 0)")],
+    "blocks_drop_last_column": [("cols = col_idx[row_ptr[i]:row_ptr[i + 1]]", "cols = col_idx[row_ptr[i]:row_ptr[i + 1] - 1]")],
+    "blocks_row_of_next_block": [("cols = col_idx[row_ptr[i]:row_ptr[i + 1]]",
+                                  "cols = col_idx[row_ptr[min(i + 1, n - 1)]:row_ptr[min(i + 1, n - 1) + 1]]")],
+    "blocks_no_condition_mask": [("mask = token_mask(rows, keys, cond_len, local, stride)",
+                                  "mask = np.ones((rows.size, keys.size), dtype=bool)")],
     "bwd_delta_sign": [("ds = p * (dp - delta[:, None])", "ds = p * (dp + delta[:, None])")],
     "bwd_delta_dropped": [("ds = p * (dp - delta[:, None])", "ds = p * dp")],
     "bwd_dq_scale": [("dq = (ds @ k) * SOFTMAX_SCALE", "dq = ds @ k")],
