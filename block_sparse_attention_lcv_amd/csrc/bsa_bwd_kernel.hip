@@ -416,6 +416,187 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   }
 }
 
+// ------------------------------------------------------------ dQ of the cross-attention
+// With at most kCrossResidentBlocks text blocks (512 tokens) a head's text K and V fit in
+// LDS (128 KB): each workgroup loads them once and streams a range of query blocks past
+// them, four per round (two wavefronts per query block, 32 rows each, as in bwd_dq_kernel).
+// The walk has no copies and no barriers, so the wavefronts run on their own; each loads its
+// next round's Q, dO, lse and D right after its walk, under its dQ stores and the partner
+// wavefront's work.  Per text block the arithmetic is bwd_dq_kernel's (no condition rule).
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(const BwdParams P) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[kCrossResidentBlocks * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[kCrossResidentBlocks * kTileBytes];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int item = xcd_item();
+  if (item >= P.bh * P.q_parts) return;
+  const int bh = item / P.q_parts;
+  const int part = item - bh * P.q_parts;
+  const int64_t base = (int64_t)bh * P.N;
+  const int key_end = key_end_of<true>(P, bh);
+  const int nkb = (key_end + 63) >> 6;   // <= kCrossResidentBlocks: kv_len is checked on the host
+  const int64_t kv_base = (int64_t)bh * P.kv_len;
+  const int blk0 = part * P.q_per_part;
+  const int blk1 = blk0 + P.q_per_part < P.n_blocks ? blk0 + P.q_per_part : P.n_blocks;
+
+  // the text blocks, rows past the item's length clamped to its last token (masked below)
+  for (int j = 0; j < nkb; ++j) {
+    copy_tile(P.k + kv_base * 64, key_end, j, lds_k + j * kTileBytes, wave, lane);
+    copy_tile(P.v + kv_base * 64, key_end, j, lds_v + j * kTileBytes, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const bf16x8 ones = ones_slots(g);
+  uint32_t ka_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
+  const uint32_t tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
+
+  // Q and dO (zeros past the range or the sequence), and lse and D (an empty row's there),
+  // of this wavefront's 32 rows of query block qb
+  auto row_ok = [&](int qb, int& qq) __attribute__((always_inline)) {
+    qq = 64 * qb + 32 * (wave & 1) + l32;
+    return qb < blk1 && qq < P.N;
+  };
+  auto load_qdo = [&](int qb, bf16x8 (&qx)[4], bf16x8 (&dx)[4]) __attribute__((always_inline)) {
+    int qq;
+    const bool ok = row_ok(qb, qq);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qx[ks] = load_chunk(P.q + base * 64, qq, 2 * ks + g, ok);
+      dx[ks] = load_chunk(P.dout + base * 64, qq, 2 * ks + g, ok);
+    }
+  };
+  auto load_stats = [&](int qb, float& l2, float& d) __attribute__((always_inline)) {
+    int qq;
+    const bool ok = row_ok(qb, qq);
+    l2 = ok ? P.lse2[base + qq] : kEmptyRowLse2;
+    d = ok ? P.delta[base + qq] : 0.f;
+  };
+
+  int qblk = blk0 + (wave >> 1);
+  bf16x8 qf[4], dof[4];
+  float lse2, dlt;
+  load_qdo(qblk, qf, dof);
+  load_stats(qblk, lse2, dlt);
+  while (qblk < blk1) {
+    const int qnext = qblk + kWaves;
+
+    const int q = 64 * qblk + 32 * (wave & 1) + l32;
+    const bf16x8 fold_d = fold_neg(dlt, g);
+    f32x16 dqt[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
+
+    auto sdp_half = [&](const unsigned char* kb, const unsigned char* vb, int kt, f32x16& s, f32x16& dp)
+        __attribute__((always_inline)) {
+      bf16x8 ka[4], va[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
+        va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
+      }
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks > 0) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dof[ks], dp, 0, 0, 0);
+      }
+    };
+    auto mask_half = [&](int j, int kt, f32x16& s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 64 * j + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        s[r] = key < key_end ? s[r] : -INFINITY;
+      }
+    };
+    auto ds_half = [&](const f32x16& s, const f32x16& dp, bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(fmaf(s[r], kScoreToLog2, -lse2)) * dp[r];
+      pack16(ds, dsb);
+    };
+    auto dq_half = [&](const unsigned char* kb, int kt, const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t so = 2048u * (2 * kt + h);
+        dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0 + so), dsb[h], dqt[0], 0, 0, 0);
+        dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1 + so), dsb[h], dqt[1], 0, 0, 0);
+      }
+    };
+    auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, auto mask_tag)
+        __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 s0, dp0, s1, dp1;
+      bf16x8 d0[2], d1[2];
+      sdp_half(kb, vb, 0, s0, dp0);
+      if (MASK) mask_half(j, 0, s0);
+      sdp_half(kb, vb, 1, s1, dp1);
+      ds_half(s0, dp0, d0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      if (MASK) mask_half(j, 1, s1);
+      dq_half(kb, 0, d0);
+      ds_half(s1, dp1, d1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+      dq_half(kb, 1, d1);
+    };
+    for (int j = 0; j < nkb; ++j) {
+      const unsigned char* kb = lds_k + j * kTileBytes;
+      const unsigned char* vb = lds_v + j * kTileBytes;
+      if (64 * j + 63 >= key_end)
+        block(kb, vb, j, std::true_type{});
+      else
+        block(kb, vb, j, std::false_type{});
+    }
+
+    // the next round's rows, loaded after the walk (holding them through it would spill):
+    // they arrive while this round's dQ is stored and the partner wavefront computes
+    bf16x8 qf_n[4], dof_n[4];
+    float lse2_n, dlt_n;
+    load_qdo(qnext, qf_n, dof_n);
+    load_stats(qnext, lse2_n, dlt_n);
+    // dQ = dQ^T / 8, rows written as 8-byte stores of 4 channels
+    if (q < P.N) {
+      uint16_t* row = P.dq + (base + q) * 64;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          uint2 pk;
+          pk.x = pack_bf16x2(dqt[dt][4 * R] * 0.125f, dqt[dt][4 * R + 1] * 0.125f);
+          pk.y = pack_bf16x2(dqt[dt][4 * R + 2] * 0.125f, dqt[dt][4 * R + 3] * 0.125f);
+          *reinterpret_cast<uint2*>(row + 32 * dt + 8 * R + 4 * g) = pk;
+        }
+    }
+    qblk = qnext;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[ks] = qf_n[ks];
+      dof[ks] = dof_n[ks];
+    }
+    lse2 = lse2_n;
+    dlt = dlt_n;
+  }
+}
+
 // ---------------------------------------------------------------------------------- dK, dV
 template <bool CROSS>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParams P) {
@@ -737,7 +918,12 @@ hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
   }
   // cross-attention; with no query (n_chunks = 0) the reduction writes dK = dV = 0
   if (p.bh_rows > 0) {
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);
+    if (p.q_parts > 0)   // the text fits in LDS
+      hipLaunchKernelGGL(bwd_dq_cross_resident_kernel, dim3(grid_for((int64_t)p.bh * p.q_parts)), dim3(kBwdThreads),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream,
+                         p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -272,6 +272,7 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
 // follow lse2 and delta in the workspace (16-byte aligned).
 struct CrossBwdPlan {
   int32_t n_q_blocks, n_kv_blocks, n_st, n_kg, n_chunks, q_chunk;
+  int32_t q_parts, q_per_part;   // query walk with the text resident in LDS (q_parts = 0: not)
   int64_t part_offset, part_floats, workspace_floats;
 };
 
@@ -291,6 +292,14 @@ CrossBwdPlan cross_bwd_plan(int64_t bh, int32_t n_q, int32_t kv_len) {
     chunks = (pl.n_q_blocks + pl.q_chunk - 1) / pl.q_chunk;   // no empty chunk
   }
   pl.n_chunks = (int32_t)chunks;
+  // query walk: with the text in LDS, about 1024 workgroups of whole rounds of 4 query blocks
+  if (pl.n_q_blocks > 0 && pl.n_kv_blocks <= lcv::kCrossResidentBlocks) {
+    int64_t parts = (1024 + bh - 1) / bh;
+    parts = parts < pl.n_st ? parts : pl.n_st;
+    const int64_t per = ((pl.n_q_blocks + parts - 1) / parts + lcv::kWaves - 1) / lcv::kWaves * lcv::kWaves;
+    pl.q_per_part = (int32_t)per;
+    pl.q_parts = (int32_t)((pl.n_q_blocks + per - 1) / per);
+  }
   pl.n_kg = (int32_t)(n_groups * chunks);
   const int64_t rows = bh * n_q;
   pl.part_offset = (2 * rows + 3) / 4 * 4;
@@ -641,6 +650,8 @@ lcv_status lcv_cross_attention_backward(const void* q, const void* k, const void
   p.n_kv_blocks = pl.n_kv_blocks;
   p.q_chunk = pl.q_chunk;
   p.n_chunks = pl.n_chunks;
+  p.q_parts = pl.q_parts;
+  p.q_per_part = pl.q_per_part;
   e = lcv::launch_bsa_bwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "cross-attention backward launch");
   return ok();

@@ -192,7 +192,11 @@ struct BwdParams {
   int32_t n_chunks;         // key-walk chunks of the query blocks
   float* part_dk;           // [n_chunks, BH, kv_len, 64] fp32 partial sums
   float* part_dv;
+  int32_t q_parts;          // > 0: query-walk workgroups per (batch, head) with the text in LDS
+  int32_t q_per_part;       // query blocks per such workgroup (a multiple of 4)
 };
+// Text blocks a cross-attention query walk keeps resident in LDS (K and V: 128 KB).
+constexpr int kCrossResidentBlocks = 8;
 
 hipError_t launch_layout_build(const LayoutRule& L, const LayoutDev& d, hipStream_t stream);
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream);

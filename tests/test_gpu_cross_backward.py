@@ -4,7 +4,9 @@ the fp64 oracle.
 The forward runs on the GPU (its bf16 output and fp32 LSE are what the backward consumes); the
 oracle differentiates the exact attention of the same bf16 inputs.  Small and medium shapes are
 compared on every element; the 720p workload on sampled query rows of every head (dq) and on
-every text key of two heads (dk, dv, each the sum over all 86,400 query rows).
+every text key of two heads (dk, dv, each the sum over all 86,400 query rows).  Texts of at
+most 512 tokens take the query walk with the text resident in LDS, longer ones the pipelined
+walk; the cases cover both and the boundary.
 
 Tolerance as for the self-attention backward, from the same arithmetic (P and dS rounded to
 bf16 for the matrix cores, K * log2(e)/8 rounded to bf16 in the key walk, D from the bf16
@@ -68,7 +70,8 @@ CASES = [
     ("one-query-one-key", 1, 2, 1, 1, None),
     ("block-exact", 1, 2, 256, 64, None),
     ("block-plus-one", 1, 2, 257, 65, None),
-    ("long-text", 1, 2, 200, 1000, None),
+    ("long-text", 1, 2, 200, 1000, None),           # past 512 text tokens: the pipelined query walk
+    ("text-513", 2, 2, 300, 513, [513, 512]),     # one token past the resident-text limit
     ("many-chunks", 1, 2, 4097, 300, [7]),        # 33 query chunks of 2 blocks, last one ragged
     ("empty-text-item", 2, 2, 130, 96, [0, 96]),
     ("lens-clamped", 2, 1, 70, 40, [-3, 99]),
