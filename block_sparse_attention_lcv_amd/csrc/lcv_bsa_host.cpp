@@ -268,8 +268,16 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
 
 // Work split of the cross-attention backward: the query walk takes four query blocks per
 // workgroup; the key walk takes four text blocks and one chunk of the query blocks, with
-// enough chunks to give the chip about 1024 workgroups; the chunks' fp32 partial dK, dV
+// enough chunks to give the chip about 512 workgroups; the chunks' fp32 partial dK, dV
 // follow lse2 and delta in the workspace (16-byte aligned).
+// workgroups the two walks of the cross-attention backward aim for (a few per compute unit)
+#ifndef LCV_CROSS_KEY_WALK_WORKGROUPS
+#define LCV_CROSS_KEY_WALK_WORKGROUPS 512
+#endif
+#ifndef LCV_CROSS_QUERY_WALK_WORKGROUPS
+#define LCV_CROSS_QUERY_WALK_WORKGROUPS 512
+#endif
+
 struct CrossBwdPlan {
   int32_t n_q_blocks, n_kv_blocks, n_st, n_kg, n_chunks, q_chunk;
   int32_t q_parts, q_per_part;   // query walk with the text resident in LDS (q_parts = 0: not)
@@ -285,16 +293,16 @@ CrossBwdPlan cross_bwd_plan(int64_t bh, int32_t n_q, int32_t kv_len) {
   int64_t chunks = 0;
   if (pl.n_q_blocks > 0 && n_groups > 0) {
     const int64_t per_chunk = bh * n_groups;
-    chunks = (1024 + per_chunk - 1) / per_chunk;
+    chunks = (LCV_CROSS_KEY_WALK_WORKGROUPS + per_chunk - 1) / per_chunk;
     chunks = chunks < 64 ? chunks : 64;
     chunks = chunks < pl.n_q_blocks ? chunks : pl.n_q_blocks;
     pl.q_chunk = (int32_t)((pl.n_q_blocks + chunks - 1) / chunks);
     chunks = (pl.n_q_blocks + pl.q_chunk - 1) / pl.q_chunk;   // no empty chunk
   }
   pl.n_chunks = (int32_t)chunks;
-  // query walk: with the text in LDS, about 1024 workgroups of whole rounds of 4 query blocks
+  // query walk: with the text in LDS, about 512 workgroups of whole rounds of 4 query blocks
   if (pl.n_q_blocks > 0 && pl.n_kv_blocks <= lcv::kCrossResidentBlocks) {
-    int64_t parts = (1024 + bh - 1) / bh;
+    int64_t parts = (LCV_CROSS_QUERY_WALK_WORKGROUPS + bh - 1) / bh;
     parts = parts < pl.n_st ? parts : pl.n_st;
     const int64_t per = ((pl.n_q_blocks + parts - 1) / parts + lcv::kWaves - 1) / lcv::kWaves * lcv::kWaves;
     pl.q_per_part = (int32_t)per;

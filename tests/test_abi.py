@@ -123,14 +123,14 @@ def test_cross_attention_argument_errors():
 
 def _cross_bwd_workspace(batch, heads, n_q, kv_len):
     """Expected scratch size: 2 values per query row (rounded up to 4), then fp32 partial dK
-    and dV per query chunk; chunks give about 1024 key-walk workgroups, at most 64 and at most
+    and dV per query chunk; chunks give about 512 key-walk workgroups, at most 64 and at most
     one per query block, none empty."""
     bh = batch * heads
     nqb, nkb = -(-n_q // 64), -(-kv_len // 64)
     groups = -(-nkb // 4)
     chunks = 0
     if nqb and groups:
-        chunks = min(-(-1024 // (bh * groups)), 64, nqb)
+        chunks = min(-(-512 // (bh * groups)), 64, nqb)
         per = -(-nqb // chunks)
         chunks = -(-nqb // per)
     return -(-2 * bh * n_q // 4) * 4 + 2 * chunks * bh * kv_len * 64
