@@ -28,3 +28,15 @@ def test_cpu_baselines_report_their_sample():
         assert r["kind"] == kind and r["unit"] == "TFLOP/s" and r["value"] > 0 and r["cores"] >= 1
         assert w.name in r["sample"]
     assert "query blocks" in blocks["sample"]
+
+
+def test_bench_refuses_several_gpus():
+    """One GPU only: asking for more exits with a message and status 2, before any GPU work."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parent.parent
+    res = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                         timeout=120, cwd=root)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr + res.stdout
