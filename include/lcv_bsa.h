@@ -39,6 +39,10 @@
  *     failures are reported as LCV_ERR_HIP.
  *   - A layout is immutable after it is built and may be shared by concurrent calls on
  *     any streams and threads.
+ *   - Every call except lcv_bsa_build_layout, lcv_bsa_layout_copy_csr and
+ *     lcv_bsa_layout_destroy only launches kernels on the given stream (no allocation,
+ *     copy, memset or synchronisation), so it may be captured into a HIP graph and
+ *     replayed; the buffers it was given stay bound to the graph.
  */
 #ifndef LCV_BSA_H
 #define LCV_BSA_H
