@@ -55,10 +55,17 @@ constexpr float kEmptyRowLse2 = 3.0e38f;   // lse * log2(e) of a row with no key
 constexpr int kWaitVm2 = 2 | (7 << 4);
 static_assert(kBwdWaves == 8, "a 64 x 64 tile is 8 wave-loads of 1 KB, one per wavefront");
 
-// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile (the forward
-// kernel's swizzle: row reads of one chunk and the transposing reads are free of bank
-// conflicts).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile.  The LDS serves
+// 256 bytes (64 banks of 4) per cycle, the 16-byte reads of 16 lanes: for one chunk in 16
+// consecutive rows, the 8 even rows and the 8 odd rows (128 bytes further on) must each take
+// 8 distinct chunk slots, so swz is a permutation of 0..7 on the even and on the odd rows of
+// every aligned group of 16 (the forward kernel's swizzle repeats every 8 rows and conflicts
+// two ways on these reads; measured 135 against 200 bytes per clock per CU).  The
+// transposing 8-byte reads stay conflict-free: bit 2 of swz(r) ^ swz(r + 2) is set on every
+// aligned group of 4 rows.
+__device__ __forceinline__ int swz(int row) {
+  return (((row & 3) << 1) | ((row >> 2) & 1)) ^ (((row >> 3) & 1) << 1);
+}
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
 }
@@ -118,29 +125,34 @@ __device__ __forceinline__ void pack16(const f32x16& x, bf16x8 (&b)[2]) {
 
 // Offsets of the transposing reads that give the A operand X^T of a contraction over the
 // rows of a row-major tile X (the rows in the order in which an accumulator holds them):
-// channel tile dt, plus 2048 * (2 * half + step) for the 16 rows of a step.
-__device__ __forceinline__ uint32_t tr_off(int lane, int dt) {
+// channel tile dt, rows 4g + (lane & 15) / 4 of a 16-row step (plus 8 for the upper half,
+// whose swizzle differs), plus 2048 * (2 * half + step) for the step (16 rows: the swizzle
+// repeats).
+struct TrOff {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ TrOff tr_off(int lane, int dt) {
   const int g = lane >> 5;
   const int row0 = 4 * g + ((lane & 15) >> 2);
   const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  return tile_off(row0, col >> 3) + (uint32_t)(lane & 1) * 8u;
+  return {tile_off(row0, col >> 3) + (uint32_t)(lane & 1) * 8u, tile_off(row0 + 8, col >> 3) + (uint32_t)(lane & 1) * 8u};
 }
 
-__device__ __forceinline__ bf16x8 tr_read(const unsigned char* tile, uint32_t off) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off + 1024u));
+__device__ __forceinline__ bf16x8 tr_read(const unsigned char* tile, const TrOff& off, uint32_t step) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off.lo + step));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off.hi + step));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Asynchronous copy of rows 64*blk .. 64*blk+63 (clamped to the sequence) of a [N, 64] bf16
 // slice into an LDS tile: wavefront w moves rows 8w .. 8w+7, lane l row 8w + l/8, landing at
-// physical chunk l%8, which holds logical chunk (l%8) ^ swz(row%8) of the swizzle.
+// physical chunk l%8, which holds logical chunk (l%8) ^ swz(row) of the swizzle.
 __device__ __forceinline__ void copy_tile(const uint16_t* slice, int32_t N, int blk, unsigned char* dst, int wave,
                                           int lane) {
   const int row = 8 * wave + (lane >> 3);
   int t = 64 * blk + row;
   t = t < N ? t : N - 1;
-  const int gch = (lane & 7) ^ swz(lane >> 3);
+  const int gch = (lane & 7) ^ swz(row);
   __builtin_amdgcn_global_load_lds(slice + (int64_t)t * 64 + 8 * gch, (lds_void*)(dst + 1024 * wave), 16, 0, 0);
 }
 
@@ -249,7 +261,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   uint32_t ka_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
-  const uint32_t tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
+  const TrOff tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
 
   f32x16 dqt[2];   // dQ^T tiles [channel tile]: lane = query, registers = channels
 #pragma unroll
@@ -319,8 +331,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t so = 2048u * (2 * kt + h);
-      dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0 + so), dsb[h], dqt[0], 0, 0, 0);
-      dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1 + so), dsb[h], dqt[1], 0, 0, 0);
+      dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0, so), dsb[h], dqt[0], 0, 0, 0);
+      dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1, so), dsb[h], dqt[1], 0, 0, 0);
     }
   };
 
@@ -455,7 +467,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
   uint32_t ka_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
-  const uint32_t tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
+  const TrOff tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
 
   // Q and dO (zeros past the range or the sequence), and lse and D (an empty row's there),
   // of this wavefront's 32 rows of query block qb
@@ -528,8 +540,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t so = 2048u * (2 * kt + h);
-        dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0 + so), dsb[h], dqt[0], 0, 0, 0);
-        dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1 + so), dsb[h], dqt[1], 0, 0, 0);
+        dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr0, so), dsb[h], dqt[0], 0, 0, 0);
+        dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, tr1, so), dsb[h], dqt[1], 0, 0, 0);
       }
     };
     auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, auto mask_tag)
@@ -645,7 +657,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   uint32_t qa_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qa_off[ks] = tile_off(l32, 2 * ks + g);
-  const uint32_t tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
+  const TrOff tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
 
   f32x16 dvt[2], dkt[2];   // dV^T, dK^T tiles [channel tile]: lane = key, registers = channels
 #pragma unroll
@@ -738,10 +750,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t so = 2048u * (2 * qt + h);
-      dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr0 + so), pb[h], dvt[0], 0, 0, 0);
-      dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr1 + so), pb[h], dvt[1], 0, 0, 0);
-      dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr0 + so), dsb[h], dkt[0], 0, 0, 0);
-      dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr1 + so), dsb[h], dkt[1], 0, 0, 0);
+      dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr0, so), pb[h], dvt[0], 0, 0, 0);
+      dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ob, tr1, so), pb[h], dvt[1], 0, 0, 0);
+      dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr0, so), dsb[h], dkt[0], 0, 0, 0);
+      dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, tr1, so), dsb[h], dkt[1], 0, 0, 0);
     }
   };
 

@@ -61,11 +61,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile; chunks are
-// XOR-swizzled by swz(row), a permutation of 0..7 over each 8 rows, so that the 16-byte
-// reads of one chunk in 8 consecutive rows hit distinct banks, and so that the transposing
-// 8-byte reads (a chunk pair of 4 consecutive rows per 16 lanes) do too: swz(row) / 2 takes
-// 4 distinct values on every aligned group of 4 rows.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR-swizzled by swz(row).  The LDS serves 256 bytes (64 banks of 4) per cycle, the 16-byte
+// reads of 16 lanes: for one chunk in 16 consecutive rows, the 8 even rows and the 8 odd
+// rows (128 bytes further on) must each take 8 distinct chunk slots, so swz is a permutation
+// of 0..7 on the even and on the odd rows of every aligned group of 16 (a swizzle that
+// repeats every 8 rows conflicts two ways on these reads).  The transposing 8-byte reads (a
+// chunk pair of 4 consecutive rows per 16 lanes) stay conflict-free: bit 2 of
+// swz(r) ^ swz(r + 2) is set on every aligned group of 4 rows.
+__device__ __forceinline__ int swz(int row) {
+  return (((row & 3) << 1) | ((row >> 2) & 1)) ^ (((row >> 3) & 1) << 1);
+}
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
 }
@@ -101,7 +106,7 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 raw, int c, const Coords& xyz,
 // Staging of K/V block j into an LDS stage.  The 8 KB tile is moved as 8 wave-loads of
 // 1 KB (8 rows); wavefront w issues loads u = w*kLoadsPerWave + c.  In load u, lane l carries
 // row 8u + l/8 and lands at LDS byte 1024u + 16l, i.e. physical chunk l%8 of that row, which
-// holds logical chunk (l%8) ^ swz(row%8) under the swizzle of tile_off.  Rows past the end
+// holds logical chunk (l%8) ^ swz(8u + l/8) under the swizzle of tile_off.  Rows past the end
 // of the sequence read row N-1 (finite data; their scores are masked and their
 // probabilities are zero).
 constexpr int kLoadsPerWave = 8 / kWaves;
@@ -155,10 +160,10 @@ __device__ __forceinline__ const uint16_t* kv_row(const KvSrc& s, bool is_k, int
 template <bool ROPE_K, bool CACHED>
 __device__ __forceinline__ void stage_issue(const KvSrc& src, unsigned char* kdst, unsigned char* vdst, int j, int wave,
                                             int lane, u32x4 (&kreg)[kLoadsPerWave]) {
-  const int gch = (lane & 7) ^ swz(lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
+    const int gch = (lane & 7) ^ swz(8 * u + (lane >> 3));
     const int key = 64 * j + 8 * u + (lane >> 3);
     const int row0 = 64 * j + 8 * u;
     const uint16_t* vsrc = kv_row<CACHED>(src, false, row0, key, gch);
@@ -174,10 +179,10 @@ __device__ __forceinline__ void stage_issue(const KvSrc& src, unsigned char* kds
 // Rotate the K chunks loaded into kreg and write them to the stage (fused K RoPE only).
 __device__ __forceinline__ void stage_store_k(const FwdParams& P, unsigned char* stage, int j, int wave, int lane,
                                               const float2* tab, const u32x4 (&kreg)[kLoadsPerWave]) {
-  const int gch = (lane & 7) ^ swz(lane >> 3);
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) {
     const int u = wave * kLoadsPerWave + c;
+    const int gch = (lane & 7) ^ swz(8 * u + (lane >> 3));
     const int key = 64 * j + 8 * u + (lane >> 3);
     u32x4 kv = kreg[c];
     if (key < P.N) kv = rope_chunk(kv, gch, token_coords((uint32_t)key, P), tab, P);
@@ -334,12 +339,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   uint32_t ka_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
-  uint32_t vb_off[2];
+  // transposing reads of V: rows krow0 (low half) and krow0 + 8 (high half, another swizzle)
+  uint32_t vb_off[2], vb_off_hi[2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt) {
     const int krow0 = 4 * g + ((lane & 15) >> 2);
     const int dcol = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     vb_off[dt] = tile_off(krow0, dcol >> 3) + (uint32_t)(lane & 1) * 8u;
+    vb_off_hi[dt] = tile_off(krow0 + 8, dcol >> 3) + (uint32_t)(lane & 1) * 8u;
   }
 
   const __bf16 one = (__bf16)1.0f, z = (__bf16)0.0f;
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4*)(vb + vb_off[dt] + js_off));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vb + vb_off[dt] + js_off + 1024u));
+            (lds_i16x4*)(vb + vb_off_hi[dt] + js_off));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
