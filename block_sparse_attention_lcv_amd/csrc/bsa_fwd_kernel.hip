@@ -20,12 +20,13 @@
 //    two wavefronts of different workgroups, whose matrix-core and vector phases overlap.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q as B), so
 //    each lane owns one query column: row statistics need only the partner lane l^32.
-//  * Online softmax in the log2 domain with a per-row reference max that only moves when a
-//    half block's probabilities grow too large (lazy rescaling).  The reference is
-//    subtracted inside the matrix-core product (one extra MFMA step), so the common score
-//    costs one v_exp_f32, half a conversion and half a dot2.  Each row's decisions
-//    depend on that row alone, so results do not depend on which other rows share the
-//    wavefront (the cached call reproduces the full call bit for bit).
+//  * Online softmax in the log2 domain with a per-row reference that only moves when a half
+//    block's probabilities grow too large (lazy rescaling), and then to a multiple of 64,
+//    so that it stays 0 for rows whose scores stay near 0; a wavefront with some nonzero
+//    reference subtracts it from its scores with the vector ALU.  The common score costs one
+//    v_exp_f32, half a conversion and half a dot2.  Each row's decisions depend on that row
+//    alone, so results do not depend on which other rows share the wavefront (the cached
+//    call reproduces the full call bit for bit).
 //  * O^T += V^T P^T with the same MFMA: P (bf16) comes straight from the S^T registers, V^T
 //    operands come from the row-major V tile through ds_read_b64_tr_b16 transposing reads.
 //  * Workgroups are numbered so that each XCD (blockIdx % 8 on MI355X) receives a
@@ -53,10 +54,15 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWavesPerSimd = LCV_WAVES_PER_SIMD;  // occupancy the register budget is sized for
 constexpr int kTileBytes = 64 * 128;            // one 64 x 64 bf16 tile
 constexpr float kScoreToLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-// Lazy rescaling: a lane's probabilities in one 32-key half (16 keys of its row) may sum to
-// at most 2^7 before the row's reference max moves, so a row's half-block sum stays <= 2^8.
-// Testing each lane on its own keeps the partner exchange out of the common path.
-constexpr float kRescaleLimit = 128.0f;
+// Lazy rescaling with a coarse reference.  A row's reference moves only when a lane's
+// probabilities in one 32-key half (16 keys of its row) sum past 2^40, and then to the
+// multiple of 64 nearest the row's largest score, which so lies within 32 of it (a row's
+// first block always sets it).  Every probability therefore stays below 2^40 and a row's sum
+// below 2^56, far inside fp32 and bf16, the largest probability of a row is at least 2^-32,
+// and a rescale multiplies by an exact power of two.  Testing each lane on its own keeps the
+// partner exchange out of the common path.
+constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
+__device__ __forceinline__ float coarse_ref(float m) { return 64.0f * __builtin_rintf(m * (1.0f / 64.0f)); }
 constexpr float kLn2 = 0.6931471805599453f;
 
 
@@ -223,21 +229,6 @@ __device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb
   return acc0 + acc1;
 }
 
-// B operand of the folded step: -m split into three bf16 parts (hi + mid + lo == -m to fp32
-// precision) in channels 0..2 of the lanes holding channel group 0.  Together with the A
-// operand of ones in the same channels, one extra MFMA step adds -m to every score.
-__device__ __forceinline__ bf16x8 fold_operand(float m, int g) {
-  const float nm = -m;
-  const __bf16 hi = (__bf16)nm;
-  const float r1 = nm - (float)hi;
-  const __bf16 mid = (__bf16)r1;
-  const __bf16 lo = (__bf16)(r1 - (float)mid);
-  const __bf16 z = (__bf16)0.0f;
-  const bf16x8 v = {hi, mid, lo, z, z, z, z, z};
-  const bf16x8 zero = {z, z, z, z, z, z, z, z};
-  return g == 0 ? v : zero;
-}
-
 // Q chunk (8 bf16 channels) -> bf16(value * log2(e)/8): the softmax scale and the change to
 // base 2 travel with Q into the matrix cores.
 __device__ __forceinline__ u32x4 scale_chunk(u32x4 raw) {
@@ -349,9 +340,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     vb_off_hi[dt] = tile_off(krow0 + 8, dcol >> 3) + (uint32_t)(lane & 1) * 8u;
   }
 
-  const __bf16 one = (__bf16)1.0f, z = (__bf16)0.0f;
-  const bf16x8 ones_a = (g == 0) ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
-
   // ---- state
   f32x16 o[2][2];   // O^T tiles [d tile][query tile]
 #pragma unroll
@@ -360,9 +348,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[a][b][r] = 0.f;
-  float mref[2] = {-INFINITY, -INFINITY};   // reference max of each row (log2 units), -inf = none yet
+  float mref[2] = {-INFINITY, -INFINITY};   // reference of each row (log2 units), -inf = none yet
   float lsum[2] = {0.f, 0.f};
-  bf16x8 mneg[2] = {fold_operand(0.f, g), fold_operand(0.f, g)};
+  bool ref_nonzero = false;                 // some row of the wavefront has a reference other than 0
 
   // the workgroup's list: layout-built (self-attention), or every text block for all four
   // wavefronts (cross-attention)
@@ -389,22 +377,36 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // S^T[key][query] - m = K Q'^T + (ones x -m) for the keys 32*kt .. 32*kt+31 of a stage
-  auto qk_half = [&](auto stage_tag, int kt, f32x16 (&s)[2]) {
+  // S^T[key][query] = K Q'^T for the keys 32*kt .. 32*kt+31 of a stage: the K operands, then
+  // the products
+  auto read_k = [&](auto stage_tag, int kt, bf16x8 (&ka)[4]) {
     const unsigned char* kb = decltype(stage_tag)::value ? lds_k1 : lds_k0;
-    bf16x8 ka[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
+  };
+  auto qk_half = [&](const bf16x8 (&ka)[4], f32x16 (&s)[2]) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       f32x16 acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, mneg[qt], acc, 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qt][ks], acc, 0, 0, 0);
       s[qt] = acc;
+    }
+  };
+  // scores relative to the rows' current references (nothing to do while every row of the
+  // wavefront keeps the reference 0, or has none yet)
+  auto rebase = [&](f32x16 (&s)[2]) {
+    if (ref_nonzero) {
+      const float f0 = (mref[0] == -INFINITY) ? 0.f : mref[0];
+      const float f1 = (mref[1] == -INFINITY) ? 0.f : mref[1];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[0][r] -= f0;
+        s[1][r] -= f1;
+      }
     }
   };
 
@@ -421,11 +423,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       }
   };
 
-  // Online softmax of one half: p = 2^(s - m) with the row's reference m already folded into
-  // s.  The reference only moves when a lane's probabilities in this half exceed the limit;
-  // the fast path is then one v_exp_f32, half a conversion and half a dot2 per score.
-  // Returns per query tile the change of the folded reference (0 when it did not move), which
-  // the caller applies to scores that were formed with the previous reference.
+  // Online softmax of one half: p = 2^(s - m) with the scores s already taken relative to
+  // the row's reference m.  The reference only moves when a lane's probabilities in this half
+  // exceed the limit; the fast path is then one v_exp_f32, half a conversion and half a dot2
+  // per score.  The slow path recomputes the half's probabilities against the moved
+  // reference (shifted by its change, delta).
   auto softmax_fast = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float (&psum)[2], bool (&trig)[2]) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -441,23 +443,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[qt][r]);
       bm = fmaxf(bm, partner(bm));
-      const float m_fold = (mref[qt] == -INFINITY) ? 0.f : mref[qt];
+      const float m_base = (mref[qt] == -INFINITY) ? 0.f : mref[qt];
       // both lanes of a row take the row's decision (the exchange runs on all lanes: under
       // a short-circuit || the triggered lanes would skip it and their partners would read
       // an inactive lane)
       const int partner_trig = __shfl_xor((int)trig[qt], 32, 64);
       const bool row_trig = trig[qt] || partner_trig != 0;
-      const float m_new = row_trig ? fmaxf(mref[qt], bm + m_fold) : mref[qt];
+      const float m_new = row_trig ? fmaxf(mref[qt], coarse_ref(bm + m_base)) : mref[qt];
       const float alpha = (m_new == mref[qt]) ? 1.f : __builtin_amdgcn_exp2f(mref[qt] - m_new);
       o[0][qt] *= alpha;
       o[1][qt] *= alpha;
       lsum[qt] *= alpha;
       mref[qt] = m_new;
-      const float m_fold_new = (m_new == -INFINITY) ? 0.f : m_new;
-      delta[qt] = m_fold - m_fold_new;
+      const float m_base_new = (m_new == -INFINITY) ? 0.f : m_new;
+      delta[qt] = m_base - m_base_new;
       psum[qt] = probs<true>(s[qt], delta[qt], pb[qt]);
-      mneg[qt] = fold_operand(m_fold_new, g);
     }
+    ref_nonzero = __any((mref[0] != 0.f && mref[0] != -INFINITY) || (mref[1] != 0.f && mref[1] != -INFINITY));
   };
 
   // O^T[d][query] += V^T P^T over the two 16-key steps of half kt; V^T operands by
@@ -483,9 +485,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 
   // One key block, its two halves software-pipelined: the second half's Q K^T is issued
   // with the first half's softmax and the first half's P V with the second half's softmax,
-  // interleaved instruction by instruction, so one wavefront keeps the matrix cores and the
-  // vector ALU busy at the same time.  A rescale of the first half (rare) shifts the second
-  // half's scores by the change of the folded reference.
+  // interleaved instruction by instruction.  Each half's scores are taken relative to the
+  // references as they stand when its softmax starts (after the first half's rescale, if any).
   auto attend = [&](auto stage_tag, auto mask_tag, int j, auto&& copies) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = 64 * j;
@@ -493,34 +494,33 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     bf16x8 p0[2][2], p1[2][2];
     float psum[2], delta[2];
     bool trig[2];
-    qk_half(stage_tag, 0, s0);
-    if (MASK) mask_half(key0, 0, s0);
+    bf16x8 ka0[4], ka1[4];
+    read_k(stage_tag, 0, ka0);
+    qk_half(ka0, s0);
+    read_k(stage_tag, 1, ka1);
     // the next block's copies go out under the first half's matrix-core work, so that the
     // loads of all wavefronts do not queue up at the start of the step
     copies();
-    qk_half(stage_tag, 1, s1);
+    // 4 K reads, the first half's 8 Q K^T MFMAs, the second half's 4 K reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if (MASK) mask_half(key0, 0, s0);
+    rebase(s0);
+    qk_half(ka1, s1);
     softmax_fast(s0, p0, psum, trig);
-    // 4 K reads, then 10 Q K^T MFMAs of the first half, then the second half's 10 MFMAs
-    // each followed by vector work of the first half's softmax
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // the second half's 8 MFMAs, each followed by vector work of the first half's softmax
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
     }
-    if (__any(trig[0] || trig[1])) {
-      softmax_slow(s0, p0, psum, trig, delta);
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s1[qt][r] += delta[qt];
-    }
+    if (__any(trig[0] || trig[1])) softmax_slow(s0, p0, psum, trig, delta);
     lsum[0] += psum[0];
     lsum[1] += psum[1];
-    pv_half(stage_tag, 0, p0);
     if (MASK) mask_half(key0, 1, s1);
+    rebase(s1);
+    pv_half(stage_tag, 0, p0);
     softmax_fast(s1, p1, psum, trig);
     // 8 V^T reads, then the first half's 8 P V MFMAs each followed by vector work of the
     // second half's softmax
