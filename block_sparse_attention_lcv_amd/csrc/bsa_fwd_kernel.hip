@@ -197,7 +197,7 @@ __device__ __forceinline__ void stage_store_k(const FwdParams& P, unsigned char*
 }
 
 // p = 2^(s + shift) for the 16 scores of query tile qt held by this lane in one 32-key half
-// (the scores already include -m through the folded MFMA step), packed to bf16 as the B
+// (the scores already taken relative to the row's reference m), packed to bf16 as the B
 // operands of the two 16-key P*V steps; returns the lane's sum of the rounded
 // probabilities.  The bf16 pairs are built as bf16x2 values and fed to the dot2 intrinsic
 // directly: taking them out of a u32 vector by bit_cast was mis-optimised by the compiler
