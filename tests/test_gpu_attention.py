@@ -107,6 +107,46 @@ def test_peaked_softmax(lib):
     assert lse_err <= 0.25, lse_err
 
 
+@pytest.mark.parametrize("offset", [3072.0, -3072.0], ids=["plus", "minus"])
+def test_score_offset_far_from_zero(lib, offset):
+    """Every score of a row shifted by the same large amount: channel 0 of every key is 1 and
+    channel 0 of every query is +-3072, so each score gains +-384 (natural units, ~ +-554 in
+    log2 units).  The softmax ignores a shift that is common to the row, so the output must
+    match the oracle within the usual bounds.  This exercises the kernel's row reference far
+    from 0 in both directions: each row's first block moves it to +-576, the subtraction runs on
+    the vector ALU, and the probabilities stay within 2^+-32 of the row's largest one.
+    The LSE carries the shift as the kernel forms it: Q times log2(e)/8 is rounded to bf16
+    (here 3072 * log2(e)/8 = 554.0 ...), so the kernel's LSE differs from the oracle's by that
+    rounding of the offset (computed below from the same float32 product and round-to-nearest-
+    even) and by the usual error otherwise.  No RoPE: a rotation would mix channel 0 into
+    channel 1 with a per-token angle and break the common shift."""
+    import torch
+    n, heads, cond, local, stride = 630, 2, 210, 2, 4
+    qb, kb, vb = qkv_bits(38, 1, heads, n)
+    q_bits = np.float32(offset).view(np.uint32) >> 16          # +-3072 is exact in bf16
+    qb = qb.copy()
+    kb = kb.copy()
+    qb[..., 0] = np.uint16(q_bits)
+    kb[..., 0] = np.uint16(np.float32(1.0).view(np.uint32) >> 16)
+    say(f"[attn] score offset {offset:+.0f} on channel 0")
+    layout = lib.build_layout(n, local, stride, cond)
+    out, lse = lib.forward(to_dev(qb), to_dev(kb), to_dev(vb), layout, grid=None)
+    _sync()
+    ref_o, ref_l = oracle.bsa_forward(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb), None,
+                                      cond, local, stride, rope_q=False, rope_k=False)
+    got = from_dev_f64(out)
+    max_abs, rel = assert_out_close(got, ref_o, f"offset {offset:+.0f}")
+    # the kernel's offset in log2 units: float32 product, then round to nearest even bf16
+    prod = np.float32(offset) * np.float32(1.4426950408889634 / 8.0)
+    bits = int(prod.view(np.uint32))
+    rounded = np.uint32((bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000).view(np.float32)
+    shift = (float(rounded) - offset * 1.4426950408889634 / 8.0) * 0.6931471805599453
+    got_l = lse.cpu().numpy().astype(np.float64)
+    lse_err = assert_lse_close(got_l - shift, ref_l, f"offset {offset:+.0f}")
+    say(f"  max_abs {max_abs:.3e} rel_l2 {rel:.3e} lse (after the offset's rounding {shift:+.4f}) {lse_err:.3e}")
+    layout.close()
+
+
 def test_batch_two(lib):
     grid = (2, 8, 24)
     say("[attn] batch 2")
