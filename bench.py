@@ -36,7 +36,7 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("bsa_fwd_kernel.hip", "lcv_internal.h", "rope_math.h")
+KERNEL_SOURCES = ("bsa_fwd_kernel.hip", "attn_tile.h", "lcv_internal.h", "rope_math.h")
 
 
 def kernel_source_hash() -> str:
@@ -281,7 +281,7 @@ def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: in
     gen = torch.Generator(device="cpu").manual_seed(13)
     do = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(2 * q.shape[0] * q.shape[1] * q.shape[2], dtype=torch.float32, device="cuda")
+    ws = torch.empty(bsa.backward_workspace(q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32, device="cuda")
     for _ in range(3):
         bsa.backward(q, k, v, out, lse, do, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
     ms = timed_launches(torch, stream,

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_INVALID_ARG", 3: "ERR_SHAPE", 5:
 EXPORTED = ("lcv_bsa_layout_query", "lcv_bsa_build_layout", "lcv_bsa_layout_get_info", "lcv_bsa_layout_copy_csr",
             "lcv_bsa_layout_destroy", "lcv_rope3d_apply", "lcv_qk_rmsnorm_rope3d",
             "lcv_qk_rmsnorm_rope3d_backward_workspace", "lcv_qk_rmsnorm_rope3d_backward", "lcv_bsa_forward",
-            "lcv_bsa_forward_cached", "lcv_bsa_forward_rows", "lcv_bsa_backward", "lcv_cross_attention",
+            "lcv_bsa_forward_cached", "lcv_bsa_forward_rows", "lcv_bsa_backward_workspace", "lcv_bsa_backward",
+            "lcv_cross_attention",
             "lcv_cross_attention_backward_workspace", "lcv_cross_attention_backward", "lcv_attn_merge",
             "lcv_last_error", "lcv_abi_version")
 
@@ -84,7 +85,8 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp]),
         "lcv_bsa_forward_rows": (i32, [vp, vp, vp, i32, i32, vp, i32, u32, ctypes.POINTER(Rope3dGrid), i32, i32, vp, vp,
                                        vp]),
-        "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp]),
+        "lcv_bsa_backward_workspace": (i64, [i32, i32, i32]),
+        "lcv_bsa_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, i64, vp]),
         "lcv_cross_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
         "lcv_cross_attention_backward_workspace": (i64, [i32, i32, i32, i32]),
         "lcv_cross_attention_backward": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64,
@@ -197,6 +199,28 @@ def _bf16(t, name: str):
     return t.data_ptr()
 
 
+def _check_shape(t, shape, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have the shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _check_f32(t, shape, name: str) -> None:
+    """A float32 output or input the library reads or writes: contiguous, on the GPU, of
+    exactly this shape (the library only receives its address)."""
+    import torch
+    _check_shape(t, shape, name)
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+
+
+def _check_devices(ref, named) -> None:
+    """Every tensor on the device of ref (the library launches on the current device and
+    receives raw addresses)."""
+    for name, t in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
 def rope3d_apply(x, grid, token_offset: int = 0, out=None, stream=None):
     """3D-RoPE of x[..., n_tokens, 64] (bf16); out may be x for in-place use."""
     import torch
@@ -270,6 +294,13 @@ def forward(q, k, v, layout: Layout, grid=None, rope_q: bool = True, rope_k: boo
     B, Hh, N, D = q.shape
     if D != 64 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share the shape [B, H, N, 64]")
+    if N != layout.n_tokens:
+        raise ValueError(f"q holds {N} tokens, the layout {layout.n_tokens}")
+    if out is not None:
+        _check_shape(out, q.shape, "out")
+    if lse is not None:
+        _check_f32(lse, (B, Hh, N), "lse")
+    _check_devices(q, (("k", k), ("v", v), ("out", out), ("lse", lse)))
     g = _as_grid(grid)
     flags = _flags(rope_q, rope_k) if g is not None else 0
     out = torch.empty_like(q) if out is None else out
@@ -292,6 +323,11 @@ def forward_rows(q_rows, k, v, layout: Layout, row_begin: int, row_end: int, gri
         raise ValueError(f"q_rows must be [B, H, {row_end - row_begin}, 64]")
     if k.shape != (B, Hh, layout.n_tokens, 64) or v.shape != k.shape:
         raise ValueError(f"k, v must be [B, H, {layout.n_tokens}, 64]")
+    if out is not None:
+        _check_shape(out, q_rows.shape, "out")
+    if lse is not None:
+        _check_f32(lse, (B, Hh, M), "lse")
+    _check_devices(q_rows, (("k", k), ("v", v), ("out", out), ("lse", lse)))
     g = _as_grid(grid)
     flags = _flags(rope_q, rope_k) if g is not None else 0
     out = torch.empty_like(q_rows) if out is None else out
@@ -316,6 +352,12 @@ def forward_cached(q_noise, k_noise, v_noise, k_cond, v_cond, layout: Layout, gr
         raise ValueError(f"noise tensors must hold N-C = {layout.n_tokens - C} tokens")
     if C > 0 and (k_cond.shape != (B, Hh, C, 64) or v_cond.shape != (B, Hh, C, 64)):
         raise ValueError("k_cond, v_cond must be [B, H, C, 64]")
+    if out is not None:
+        _check_shape(out, q_noise.shape, "out")
+    if lse is not None:
+        _check_f32(lse, (B, Hh, M), "lse")
+    _check_devices(q_noise, (("k_noise", k_noise), ("v_noise", v_noise), ("k_cond", k_cond if C > 0 else None),
+                             ("v_cond", v_cond if C > 0 else None), ("out", out), ("lse", lse)))
     g = _as_grid(grid)
     flags = _flags(rope_q, rope_k) if g is not None else 0
     out = torch.empty_like(q_noise) if out is None else out
@@ -341,22 +383,35 @@ def backward(q, k, v, out, lse, dout, layout: Layout, dq=None, dk=None, dv=None,
             raise ValueError(f"{name} must have the shape of q [B, H, N, 64]")
     if D != 64 or N != layout.n_tokens:
         raise ValueError(f"q must be [B, H, {layout.n_tokens}, 64]")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None and t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
     if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or lse.shape != (B, Hh, N):
         raise ValueError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape:
-            raise ValueError(f"{name} must have the shape of q")
+    _check_devices(q, (("k", k), ("v", v), ("out", out), ("lse", lse), ("dout", dout), ("dq", dq), ("dk", dk),
+                       ("dv", dv), ("workspace", workspace)))
+    need = backward_workspace(B, Hh, N)
     if workspace is None:
-        workspace = torch.empty(2 * B * Hh * N, dtype=torch.float32, device=q.device)
-    if workspace.dtype != torch.float32 or not workspace.is_cuda or workspace.numel() < 2 * B * Hh * N:
-        raise ValueError("workspace must be a float32 CUDA tensor of at least 2 * B * H * N values")
+        workspace = torch.empty(need, dtype=torch.float32, device=q.device)
+    if (workspace.dtype != torch.float32 or not workspace.is_cuda or not workspace.is_contiguous()
+            or workspace.numel() < need):
+        raise ValueError(f"workspace must be a contiguous float32 CUDA tensor of at least {need} values")
     _check(lib().lcv_bsa_backward(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(out, "out"), lse.data_ptr(),
                                   _bf16(dout, "dout"), B, Hh, layout.handle, layout.cond_len, _bf16(dq, "dq"),
-                                  _bf16(dk, "dk"), _bf16(dv, "dv"), workspace.data_ptr(), _stream_ptr(stream)))
+                                  _bf16(dk, "dk"), _bf16(dv, "dv"), workspace.data_ptr(), workspace.numel(),
+                                  _stream_ptr(stream)))
     return dq, dk, dv
+
+
+def backward_workspace(batch: int, heads: int, n_tokens: int) -> int:
+    """fp32 values of scratch that backward needs for these sizes."""
+    n = lib().lcv_bsa_backward_workspace(batch, heads, n_tokens)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return n
 
 
 def cross_attention(q, k, v, kv_lens=None, out=None, lse=None, with_lse: bool = True, stream=None):
@@ -373,6 +428,9 @@ def cross_attention(q, k, v, kv_lens=None, out=None, lse=None, with_lse: bool = 
     out = torch.empty_like(q) if out is None else out
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _check_f32(lse, (B, Hh, N), "lse")
+    _check_devices(q, (("k", k), ("v", v), ("out", out), ("lse", lse), ("kv_lens", kv_lens)))
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
     def ptr(t, name):   # tensors without rows may be empty (NULL)
@@ -416,6 +474,8 @@ def cross_attention_backward(q, k, v, out, lse, dout, kv_lens=None, dq=None, dk=
     dv = torch.empty_like(v) if dv is None else dv
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
         raise ValueError("dq must have the shape of q, dk and dv that of k")
+    _check_devices(q, (("k", k), ("v", v), ("out", out), ("lse", lse), ("dout", dout), ("kv_lens", kv_lens),
+                       ("dq", dq), ("dk", dk), ("dv", dv), ("workspace", workspace)))
     need = cross_attention_backward_workspace(B, Hh, N, L)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.float32, device=q.device)

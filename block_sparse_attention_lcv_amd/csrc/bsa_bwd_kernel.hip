@@ -6,20 +6,25 @@
 // With P = exp(S - lse) recomputed from the saved LSE, the gradients are
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D) with D = rowsum(dO * O),
 //   dQ = dS K / 8, dK = dS^T Q / 8.
+// Both walks score with the forward's own operands: Q' = bf16(Q * log2(e)/8), rounded as the
+// forward rounds it, against the unscaled K, so that P = exp2(S' - lse * log2(e)) is the
+// forward's probability of the pair (up to the order of the fp32 additions) and agrees with
+// the forward's LSE however large the scores.  With S' = Q' K^T the forward's score in log2
+// units, dS/dK = Q' ln 2 (the derivative of that score in natural units) and dS/dQ = K / 8.
 // Three kernels:
-//  * bwd_prep_kernel: D and lse * log2(e) per row (HBM-bound, one pass over O and dO);
+//  * bwd_prep_kernel: D = rowsum(dO * O), lse * log2(e) and Q' per row (HBM-bound, one pass
+//    over Q, O and dO) into the workspace;
 //  * bwd_dq_kernel: the row walk of the forward -- a workgroup of 8 wavefronts owns 4 query
 //    blocks (32 rows per wavefront) and streams the K and V blocks of their rows through LDS;
-//    per 32-key half it forms S^T = K Q^T and dP^T = V dO^T with v_mfma_f32_32x32x16_bf16
-//    (D folded into one extra MFMA step, as the forward folds its row max; the row's lse is
-//    the lane's own and enters through the FMA that scales the score), then dS^T and
-//    dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16;
+//    per 32-key half it forms S^T - lse * log2(e) = K Q'^T and dP^T - D = V dO^T with
+//    v_mfma_f32_32x32x16_bf16 (the row's lse and D are folded into one extra MFMA step each),
+//    then dS^T = exp2(.) (dP^T - D) and dQ^T += K^T dS^T with K^T read through
+//    ds_read_b64_tr_b16;
 //  * bwd_dkdv_kernel: the column walk -- a workgroup owns 4 key blocks (32 keys per
 //    wavefront) grouped so that their columns nearly coincide (the strided global blocks
-//    together) and streams the Q and dO blocks, lse and D of the union of their columns;
-//    S = Q K'^T with K' = K * log2(e)/8 rounded to bf16 (the forward scales Q the same way),
-//    so that with lse * log2(e) and D folded into one MFMA step each P = exp2(S) takes no
-//    vector work before the exponential; then dV^T += dO^T P and dK^T += Q^T dS.
+//    together) and streams the Q' and dO blocks, lse and D of the union of their columns;
+//    S' - lse * log2(e) = Q' K^T and dP - D (both folds one MFMA step), P = exp2(.) with no
+//    vector work before the exponential; then dV^T += dO^T P and dK^T += Q'^T dS.
 // Every output row is written by exactly one wavefront, with no atomics: results are
 // deterministic.
 // Cross-attention (CROSS = true): keys and values are the text states [BH, kv_len, 64] with a
@@ -29,46 +34,22 @@
 // chunk order (deterministic).
 #include <type_traits>
 
+#include "attn_tile.h"
 #include "lcv_internal.h"
-#include "rope_math.h"
 
 namespace lcv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 // read-only schedule tables through the constant address space: uniform indexes become scalar
 // loads, which neither occupy the vector memory counter nor need a readfirstlane
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 constexpr int kBwdWaves = 2 * kWaves;         // two wavefronts (32 rows each) per 64-row block
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kTileBytes = 64 * 128;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kScoreToLog2 = kLog2e / 8.0f;
 constexpr float kEmptyRowLse2 = 3.0e38f;   // lse * log2(e) of a row with no key: p = 0
 // s_waitcnt operand: vmcnt <= 2 and lgkmcnt == 0, expcnt not waited for (gfx9 field layout)
 constexpr int kWaitVm2 = 2 | (7 << 4);
 static_assert(kBwdWaves == 8, "a 64 x 64 tile is 8 wave-loads of 1 KB, one per wavefront");
-
-// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile.  The LDS serves
-// 256 bytes (64 banks of 4) per cycle, the 16-byte reads of 16 lanes: for one chunk in 16
-// consecutive rows, the 8 even rows and the 8 odd rows (128 bytes further on) must each take
-// 8 distinct chunk slots, so swz is a permutation of 0..7 on the even and on the odd rows of
-// every aligned group of 16 (the forward kernel's swizzle repeats every 8 rows and conflicts
-// two ways on these reads; measured 135 against 200 bytes per clock per CU).  The
-// transposing 8-byte reads stay conflict-free: bit 2 of swz(r) ^ swz(r + 2) is set on every
-// aligned group of 4 rows.
-__device__ __forceinline__ int swz(int row) {
-  return (((row & 3) << 1) | ((row >> 2) & 1)) ^ (((row >> 3) & 1) << 1);
-}
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
-}
 
 // fp32 value m as three bf16 parts (hi + mid + lo == m to fp32 precision) in slots 0..2 of
 // the lanes of channel group 0: with an operand of ones in the same slots, one MFMA step
@@ -90,20 +71,11 @@ __device__ __forceinline__ bf16x8 ones_slots(int g) {
   return g == 0 ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
 }
 
-// 8 channels (chunk c) of row `row` of a [rows, 64] bf16 tensor as an MFMA operand,
-// optionally times log2(e)/8 (rounded to bf16); zero when !ok.
-__device__ __forceinline__ bf16x8 load_chunk(const uint16_t* base, int64_t row, int c, bool ok,
-                                             bool scale = false) {
+// 8 channels (chunk c) of row `row` of a [rows, 64] bf16 tensor as an MFMA operand; zero
+// when !ok.
+__device__ __forceinline__ bf16x8 load_chunk(const uint16_t* base, int64_t row, int c, bool ok) {
   u32x4 raw{0u, 0u, 0u, 0u};
-  if (ok) {
-    raw = *reinterpret_cast<const u32x4*>(base + row * 64 + 8 * c);
-    if (scale) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        raw[e] = pack_bf16x2(__uint_as_float(raw[e] << 16) * kScoreToLog2,
-                             __uint_as_float(raw[e] & 0xffff0000u) * kScoreToLog2);
-    }
-  }
+  if (ok) raw = *reinterpret_cast<const u32x4*>(base + row * 64 + 8 * c);
   return __builtin_bit_cast(bf16x8, raw);
 }
 
@@ -163,15 +135,19 @@ __device__ __forceinline__ void copy_rows_f32(const float* slice, int32_t N, int
   __builtin_amdgcn_global_load_lds(slice + t, (lds_void*)dst, 4, 0, 0);
 }
 
-// D = rowsum(dO * O) and lse * log2(e) per row; one thread per 8-channel chunk of a row.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* out, const uint16_t* dout, const float* lse,
-                                                       float* lse2, float* delta, int64_t rows) {
+// D = rowsum(dO * O), lse * log2(e) and Q' = bf16(Q * log2(e)/8) per row; one thread per
+// 8-channel chunk of a row.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* q, const uint16_t* out, const uint16_t* dout,
+                                                       const float* lse, uint16_t* qs, float* lse2, float* delta,
+                                                       int64_t rows) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid >> 3;
   const int c = (int)(gid & 7);
   if (row >= rows) return;   // the eight lanes of a row leave together
+  const u32x4 qc = *reinterpret_cast<const u32x4*>(q + row * 64 + 8 * c);
   const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * 64 + 8 * c);
   const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * 64 + 8 * c);
+  *reinterpret_cast<u32x4*>(qs + row * 64 + 8 * c) = scale_chunk_log2(qc);
   float s = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -247,13 +223,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   bf16x8 qf[4], dof[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    qf[ks] = load_chunk(P.q + base * 64, q, 2 * ks + g, qok);
+    qf[ks] = load_chunk(P.qs + base * 64, q, 2 * ks + g, qok);
     dof[ks] = load_chunk(P.dout + base * 64, q, 2 * ks + g, qok);
   }
-  // the row's lse (log2 units) enters each exponent through one FMA (it is the lane's own
-  // constant); D is folded into the dP^T accumulator by one extra MFMA step
+  // the row's lse (log2 units) and D are folded into the S^T and dP^T accumulators by one
+  // extra MFMA step each
   const float lse2 = qok ? P.lse2[base + q] : kEmptyRowLse2;
   const float dlt = qok ? P.delta[base + q] : 0.f;
+  const bf16x8 fold_l = fold_neg(lse2, g);
   const bf16x8 fold_d = fold_neg(dlt, g);
   const int key_end = key_end_of<CROSS>(P, bh);                 // keys [0, key_end) exist
   const int64_t kv_base = (int64_t)bh * (CROSS ? P.kv_len : P.N);
@@ -304,10 +281,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
       va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
     }
     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks > 0) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dof[ks], dp, 0, 0, 0);
     }
   };
@@ -323,7 +300,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   auto ds_half = [&](const f32x16& s, const f32x16& dp, bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
     f32x16 ds;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(fmaf(s[r], kScoreToLog2, -lse2)) * dp[r];
+    for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(s[r]) * dp[r];
     pack16(ds, dsb);
   };
   // dQ^T += K^T dS^T over the two 16-key steps of half kt
@@ -349,13 +326,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
     copies();
     sdp_half(kb, vb, 1, s1, dp1);
     ds_half(s0, dp0, d0);
-    // 8 K/V reads, then the second half's 9 MFMAs each followed by vector work of the first
+    // 8 K/V reads, then the second half's 10 MFMAs each followed by vector work of the first
     // half's dS^T
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
+    for (int i = 0; i < 10; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     if (MASK) mask_half(j, 1, s1);
     dq_half(kb, 0, d0);
@@ -480,7 +457,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     const bool ok = row_ok(qb, qq);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qx[ks] = load_chunk(P.q + base * 64, qq, 2 * ks + g, ok);
+      qx[ks] = load_chunk(P.qs + base * 64, qq, 2 * ks + g, ok);
       dx[ks] = load_chunk(P.dout + base * 64, qq, 2 * ks + g, ok);
     }
   };
@@ -500,6 +477,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     const int qnext = qblk + kWaves;
 
     const int q = 64 * qblk + 32 * (wave & 1) + l32;
+    const bf16x8 fold_l = fold_neg(lse2, g);
     const bf16x8 fold_d = fold_neg(dlt, g);
     f32x16 dqt[2];
 #pragma unroll
@@ -516,10 +494,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
         va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
       }
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        if (ks > 0) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dof[ks], dp, 0, 0, 0);
       }
     };
@@ -533,7 +511,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     auto ds_half = [&](const f32x16& s, const f32x16& dp, bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
       f32x16 ds;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(fmaf(s[r], kScoreToLog2, -lse2)) * dp[r];
+      for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(s[r]) * dp[r];
       pack16(ds, dsb);
     };
     auto dq_half = [&](const unsigned char* kb, int kt, const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
@@ -555,9 +533,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
       ds_half(s0, dp0, d0);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < 9; ++i) {
+      for (int i = 0; i < 10; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       if (MASK) mask_half(j, 1, s1);
       dq_half(kb, 0, d0);
@@ -650,7 +628,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   bf16x8 kf[4], vf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = load_chunk(P.k + kv_base * 64, key, 2 * ks + g, kok, true);
+    kf[ks] = load_chunk(P.k + kv_base * 64, key, 2 * ks + g, kok);
     vf[ks] = load_chunk(P.v + kv_base * 64, key, 2 * ks + g, kok);
   }
   const bf16x8 ones = ones_slots(g);
@@ -685,7 +663,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     else
       return ents[e];
   };
-  const uint16_t* qslice = P.q + base * 64;
+  const uint16_t* qslice = P.qs + base * 64;
   const uint16_t* oslice = P.dout + base * 64;
   const float* lslice = P.lse2 + base;
   const float* dslice = P.delta + base;
@@ -704,7 +682,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // S' - lse * log2(e) (S' = Q K'^T, log2 units) and dP - D for queries 32qt .. 32qt+31 (registers) and the wavefront's keys
+  // S' - lse * log2(e) (S' = Q' K^T, log2 units) and dP - D for queries 32qt .. 32qt+31 (registers) and the wavefront's keys
   // (lanes); the per-query lse and D enter through one folded MFMA step each
   auto sdp_half = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int qt,
                       f32x16& s, f32x16& dp) __attribute__((always_inline)) {
@@ -744,7 +722,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     pack16(p, pb);
     pack16(ds, dsb);
   };
-  // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query steps of half qt
+  // dV^T += dO^T P and dK^T += Q'^T dS over the two 16-query steps of half qt
   auto upd_half = [&](const unsigned char* qb, const unsigned char* ob, int qt, const bf16x8 (&pb)[2],
                       const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -827,7 +805,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   if (e < cnt) step(std::integral_constant<int, 0>{}, e);
 
   if constexpr (CROSS) {
-    // fp32 partial sums of this chunk, dK already divided by 8: [chunk, BH, kv_len, 64]
+    // fp32 partial sums of this chunk, dK already scaled by ln 2: [chunk, BH, kv_len, 64]
     if (kok) {
       const int64_t prow = ((int64_t)chunk * P.bh + bh) * P.kv_len + key;
       float* krow = P.part_dk + prow * 64;
@@ -836,8 +814,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
-          const float4 k4 = {dkt[dt][4 * R] * 0.125f, dkt[dt][4 * R + 1] * 0.125f, dkt[dt][4 * R + 2] * 0.125f,
-                             dkt[dt][4 * R + 3] * 0.125f};
+          const float4 k4 = {dkt[dt][4 * R] * kLn2, dkt[dt][4 * R + 1] * kLn2, dkt[dt][4 * R + 2] * kLn2,
+                             dkt[dt][4 * R + 3] * kLn2};
           const float4 v4 = {dvt[dt][4 * R], dvt[dt][4 * R + 1], dvt[dt][4 * R + 2], dvt[dt][4 * R + 3]};
           *reinterpret_cast<float4*>(krow + 32 * dt + 8 * R + 4 * g) = k4;
           *reinterpret_cast<float4*>(vrow + 32 * dt + 8 * R + 4 * g) = v4;
@@ -845,7 +823,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     }
     return;
   }
-  // dK = dK^T / 8, dV = dV^T; key rows written as 8-byte stores of 4 channels
+  // dK = dK^T ln 2 (Q' carries log2(e)/8), dV = dV^T; key rows written as 8-byte stores of 4
+  // channels
   if (kok) {
     uint16_t* krow = P.dk + (base + key) * 64;
     uint16_t* vrow = P.dv + (base + key) * 64;
@@ -854,8 +833,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
         uint2 pk, pv;
-        pk.x = pack_bf16x2(dkt[dt][4 * R] * 0.125f, dkt[dt][4 * R + 1] * 0.125f);
-        pk.y = pack_bf16x2(dkt[dt][4 * R + 2] * 0.125f, dkt[dt][4 * R + 3] * 0.125f);
+        pk.x = pack_bf16x2(dkt[dt][4 * R] * kLn2, dkt[dt][4 * R + 1] * kLn2);
+        pk.y = pack_bf16x2(dkt[dt][4 * R + 2] * kLn2, dkt[dt][4 * R + 3] * kLn2);
         pv.x = pack_bf16x2(dvt[dt][4 * R], dvt[dt][4 * R + 1]);
         pv.y = pack_bf16x2(dvt[dt][4 * R + 2], dvt[dt][4 * R + 3]);
         *reinterpret_cast<uint2*>(krow + 32 * dt + 8 * R + 4 * g) = pk;
@@ -909,12 +888,12 @@ unsigned grid_for(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 }  // namespace
 
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
-  const bool cross = p.part_dk != nullptr;
+  const bool cross = p.cross;
   hipError_t e = hipSuccess;
   if (p.bh_rows > 0) {
     const int64_t threads = p.bh_rows * 8;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.out, p.dout,
-                       p.lse, p.lse2, p.delta, p.bh_rows);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.q, p.out,
+                       p.dout, p.lse, p.qs, p.lse2, p.delta, p.bh_rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (!cross) {

@@ -34,26 +34,19 @@
 //    in that XCD's L2.
 #include <type_traits>
 
+#include "attn_tile.h"
 #include "lcv_internal.h"
-#include "rope_math.h"
 
 namespace lcv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 64 * kWaves;
 #ifndef LCV_WAVES_PER_SIMD
 #define LCV_WAVES_PER_SIMD 2
 #endif
 constexpr int kWavesPerSimd = LCV_WAVES_PER_SIMD;  // occupancy the register budget is sized for
-constexpr int kTileBytes = 64 * 128;            // one 64 x 64 bf16 tile
-constexpr float kScoreToLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 // Lazy rescaling with a coarse reference.  A row's reference moves only when a lane's
 // probabilities in one 32-key half (16 keys of its row) sum past 2^40, and then to the
 // multiple of 64 nearest the row's largest score, which so lies within 32 of it (a row's
@@ -63,23 +56,6 @@ constexpr float kScoreToLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64
 // partner exchange out of the common path.
 constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
 __device__ __forceinline__ float coarse_ref(float m) { return 64.0f * __builtin_rintf(m * (1.0f / 64.0f)); }
-constexpr float kLn2 = 0.6931471805599453f;
-
-
-// Byte offset of 16-byte chunk `chunk` of row `row` in a 64 x 64 bf16 tile; chunks are
-// XOR-swizzled by swz(row).  The LDS serves 256 bytes (64 banks of 4) per cycle, the 16-byte
-// reads of 16 lanes: for one chunk in 16 consecutive rows, the 8 even rows and the 8 odd
-// rows (128 bytes further on) must each take 8 distinct chunk slots, so swz is a permutation
-// of 0..7 on the even and on the odd rows of every aligned group of 16 (a swizzle that
-// repeats every 8 rows conflicts two ways on these reads).  The transposing 8-byte reads (a
-// chunk pair of 4 consecutive rows per 16 lanes) stay conflict-free: bit 2 of
-// swz(r) ^ swz(r + 2) is set on every aligned group of 4 rows.
-__device__ __forceinline__ int swz(int row) {
-  return (((row & 3) << 1) | ((row >> 2) & 1)) ^ (((row >> 3) & 1) << 1);
-}
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
-}
 
 __device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -117,8 +93,6 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 raw, int c, const Coords& xyz,
 // probabilities are zero).
 constexpr int kLoadsPerWave = 8 / kWaves;
 static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Where the rows of one (batch, head)'s keys and values live, as byte addresses of key row 0
 // (wave-uniform, computed once): key row `key` is at cond + 128 key when key < split (the
@@ -229,18 +203,6 @@ __device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb
   return acc0 + acc1;
 }
 
-// Q chunk (8 bf16 channels) -> bf16(value * log2(e)/8): the softmax scale and the change to
-// base 2 travel with Q into the matrix cores.
-__device__ __forceinline__ u32x4 scale_chunk(u32x4 raw) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = __uint_as_float(raw[e] << 16) * kScoreToLog2;
-    const float b = __uint_as_float(raw[e] & 0xffff0000u) * kScoreToLog2;
-    raw[e] = pack_bf16x2(a, b);
-  }
-  return raw;
-}
-
 // CROSS: cross-attention of the video queries over text keys/values [BH, kv_len, 64]: every
 // query block attends every text block (dense, no RoPE, no condition rule), keys past the
 // batch item's text length are masked.
@@ -320,7 +282,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       if (qok[qt]) {
         raw = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
         if constexpr (ROPE_Q) raw = rope_chunk(raw, c, xyz, tab, P);
-        raw = scale_chunk(raw);
+        raw = scale_chunk_log2(raw);
       }
       qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
     }

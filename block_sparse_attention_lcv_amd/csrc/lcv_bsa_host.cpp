@@ -266,10 +266,14 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
   return ok();
 }
 
+// Workspace of the attention backward, per query row: Q' = bf16(q * log2(e)/8) (64 bf16 = 32
+// fp32 slots), then lse * log2(e) and D = rowsum(dO * O) of every row.
+constexpr int64_t kBwdRowFloats = 34;
+
 // Work split of the cross-attention backward: the query walk takes four query blocks per
 // workgroup; the key walk takes four text blocks and one chunk of the query blocks, with
 // enough chunks to give the chip about 512 workgroups; the chunks' fp32 partial dK, dV
-// follow lse2 and delta in the workspace (16-byte aligned).
+// follow the per-row values in the workspace (16-byte aligned).
 // workgroups the two walks of the cross-attention backward aim for (a few per compute unit)
 #ifndef LCV_CROSS_KEY_WALK_WORKGROUPS
 #define LCV_CROSS_KEY_WALK_WORKGROUPS 512
@@ -310,7 +314,7 @@ CrossBwdPlan cross_bwd_plan(int64_t bh, int32_t n_q, int32_t kv_len) {
   }
   pl.n_kg = (int32_t)(n_groups * chunks);
   const int64_t rows = bh * n_q;
-  pl.part_offset = (2 * rows + 3) / 4 * 4;
+  pl.part_offset = (kBwdRowFloats * rows + 3) / 4 * 4;
   pl.part_floats = chunks * bh * kv_len * 64;
   pl.workspace_floats = pl.part_offset + 2 * pl.part_floats;
   return pl;
@@ -638,8 +642,10 @@ lcv_status lcv_cross_attention_backward(const void* q, const void* k, const void
   p.out = static_cast<const uint16_t*>(out);
   p.dout = static_cast<const uint16_t*>(dout);
   p.lse = lse;
-  p.lse2 = workspace;
-  p.delta = workspace + bh * n_q;
+  p.qs = reinterpret_cast<uint16_t*>(workspace);
+  p.lse2 = workspace + 32 * bh * n_q;
+  p.delta = p.lse2 + bh * n_q;
+  p.cross = true;
   p.part_dk = workspace + pl.part_offset;
   p.part_dv = p.part_dk + pl.part_floats;
   p.dq = static_cast<uint16_t*>(dq);
@@ -665,9 +671,15 @@ lcv_status lcv_cross_attention_backward(const void* q, const void* k, const void
   return ok();
 }
 
+int64_t lcv_bsa_backward_workspace(int32_t batch, int32_t heads, int32_t n_tokens) {
+  if (batch < 1 || heads < 1 || n_tokens < 1) return -1;
+  return kBwdRowFloats * batch * heads * (int64_t)n_tokens;
+}
+
 lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
                             const void* dout, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
-                            int32_t cond_len, void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {
+                            int32_t cond_len, void* dq, void* dk, void* dv, float* workspace, int64_t workspace_floats,
+                            hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr || layout == nullptr)
     return fail(LCV_ERR_NULL, "every tensor, the workspace and the layout are required");
@@ -677,12 +689,17 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
   for (const void* t : {q, k, v, out, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv)})
     if (!aligned(t, 16)) return fail(LCV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
-  if (!aligned(lse, 4) || !aligned(workspace, 4)) return fail(LCV_ERR_INVALID_ARG, "lse and workspace must be 4-byte aligned");
+  if (!aligned(lse, 4) || !aligned(workspace, 16))
+    return fail(LCV_ERR_INVALID_ARG, "lse must be 4-byte and workspace 16-byte aligned");
   const int64_t bh = (int64_t)batch * heads;
   const int32_t N = layout->info.n_tokens;
   const int64_t items = bh * (layout->dev.n_st > layout->dev.n_kg ? layout->dev.n_st : layout->dev.n_kg);
   if (bh >= (int64_t(1) << 31) || items >= (int64_t(1) << 31) - 8 || bh * N * 8 >= (int64_t(1) << 40))
     return fail(LCV_ERR_UNSUPPORTED, "batch * heads = %lld is too large", (long long)bh);
+  const int64_t need = kBwdRowFloats * bh * N;
+  if (workspace_floats < need)
+    return fail(LCV_ERR_INVALID_ARG, "workspace holds %lld values, %lld are needed", (long long)workspace_floats,
+                (long long)need);
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -696,8 +713,10 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
   p.out = static_cast<const uint16_t*>(out);
   p.dout = static_cast<const uint16_t*>(dout);
   p.lse = lse;
-  p.lse2 = workspace;
-  p.delta = workspace + bh * N;
+  p.qs = reinterpret_cast<uint16_t*>(workspace);
+  p.lse2 = workspace + 32 * bh * N;
+  p.delta = p.lse2 + bh * N;
+  p.cross = false;
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);

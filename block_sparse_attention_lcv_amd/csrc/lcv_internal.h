@@ -169,6 +169,7 @@ struct BwdParams {
   const uint16_t* out;      // forward output
   const uint16_t* dout;     // upstream gradient
   const float* lse;         // [BH, N] natural-log LSE of the forward
+  uint16_t* qs;             // [BH, N, 64] workspace: Q' = bf16(q * log2(e)/8), the forward's operand
   float* lse2;              // [BH, N] workspace: lse * log2(e) (3e38 for an empty row)
   float* delta;             // [BH, N] workspace: rowsum(dout * out)
   uint16_t* dq;
@@ -183,7 +184,8 @@ struct BwdParams {
   const int32_t* kg_ent;
   int64_t bh_rows;          // BH * N
   int32_t N, C, n_blocks, n_st, n_kg, bh;
-  // cross-attention (text keys/values [BH, kv_len, 64]); part_dk != nullptr selects it
+  // cross-attention (text keys/values [BH, kv_len, 64])
+  bool cross;               // true: the cross-attention backward (the fields below), false: self-attention
   int32_t kv_len;           // rows per (batch, head) of k and v
   const int32_t* kv_lens;   // [B] valid text tokens, or nullptr
   int32_t heads;

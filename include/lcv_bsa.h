@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 8
+#define LCV_BSA_ABI_VERSION 9
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -220,20 +220,26 @@ lcv_status lcv_qk_rmsnorm_rope3d_backward(const void* x, const void* dy, const f
  * gradient dout, for training (myzaker article, technical principles: the LoRA-trained
  * refinement expert; SimpleTuner quickstart "LongCat-Video Edit").  With P recomputed from
  * the saved LSE: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)), dQ = dS K / 8,
- * dK = dS^T Q / 8, under the same layout and condition rule as the forward.
+ * dK = dS^T Q / 8, under the same layout and condition rule as the forward.  P is formed
+ * from the forward's own score operands (Q rounded to bf16 after its scaling by
+ * log2(e)/8, as the forward rounds it), so it agrees with the saved LSE for any score size;
+ * dK takes that same rounded Q.
  *   q, k, v, out, dout : bf16 [batch, heads, N, 64]; q and k as they entered the scores (a
  *                        caller that rotates with RoPE passes the rotated tensors and
  *                        rotates dq, dk back), out the forward's output
  *   lse                : fp32 [batch, heads, N], the forward's
  *   dq, dk, dv         : bf16 [batch, heads, N, 64], written completely (fp32 accumulation)
- *   workspace          : fp32 [2 * batch * heads * N] scratch, caller-owned (8 B per row)
+ *   workspace          : fp32 scratch, caller-owned, 16-byte aligned, at least
+ *                        lcv_bsa_backward_workspace(batch, heads, N) values (136 B per query
+ *                        row: the scaled Q and two per-row terms; -1 for invalid sizes)
  * Deterministic: every output row is written once, without atomics.  Asynchronous on
- * stream.  Errors: NULL, INVALID_ARG (sizes, alignment, device), LAYOUT_MISMATCH (cond_len),
- * UNSUPPORTED (sizes), HIP. */
+ * stream.  Errors: NULL, INVALID_ARG (sizes, alignment, device, small workspace),
+ * LAYOUT_MISMATCH (cond_len), UNSUPPORTED (sizes), HIP. */
+int64_t lcv_bsa_backward_workspace(int32_t batch, int32_t heads, int32_t n_tokens);
 lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
                             const void* dout, int32_t batch, int32_t heads, const lcv_bsa_layout* layout,
                             int32_t cond_len, void* dq, void* dk, void* dv, float* workspace,
-                            hipStream_t stream);
+                            int64_t workspace_floats, hipStream_t stream);
 
 /* Cross-attention of the video tokens over text states, the second attention of every DiT
  * block (myzaker article, technical principles: each block has 3D self-attention,
@@ -257,7 +263,8 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
  * technical principles: each block has 3D self-attention, cross-attention and a SwiGLU
  * feed-forward network; the LoRA-trained refinement expert).  With P recomputed from the
  * saved LSE over the valid text keys: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
- * dQ = dS K / 8, dK = dS^T Q / 8.
+ * dQ = dS K / 8, dK = dS^T Q / 8 (P and dK from the forward's rounded scaled Q, as in
+ * lcv_bsa_backward).
  *   q, out, dout : bf16 [batch, heads, n_q, 64];  lse : fp32 [batch, heads, n_q], the forward's
  *   k, v         : bf16 [batch, heads, kv_len, 64];  kv_lens as in lcv_cross_attention
  *   dq           : bf16 [batch, heads, n_q, 64];  dk, dv : bf16 [batch, heads, kv_len, 64];
@@ -265,8 +272,8 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
  *                  get zeros)
  *   workspace    : fp32, caller-owned, 16-byte aligned, at least
  *                  lcv_cross_attention_backward_workspace(batch, heads, n_q, kv_len) values
- *                  (per-row terms and the fp32 partial dK, dV of the query chunks; -1 for
- *                  invalid sizes)
+ *                  (the scaled Q and two per-row terms, 136 B per query row, and the fp32
+ *                  partial dK, dV of the query chunks; -1 for invalid sizes)
  * With n_q = 0 (dk = dv = 0) the query-side pointers, with kv_len = 0 (dq = 0) the text-side
  * pointers, and a workspace of size 0 may be NULL.
  * Deterministic: the chunks' partial sums are added in a fixed order, without atomics.

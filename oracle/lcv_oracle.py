@@ -100,7 +100,7 @@ def rope3d_at(x: np.ndarray, tokens: np.ndarray, grid, theta: float = 10000.0) -
     return out
 
 
-# --------------------------------------------------------------------------- layout
+# --------------------------------------------------------------------------- QK prologue (RMSNorm + RoPE)
 def rmsnorm(x: np.ndarray, gamma, eps: float) -> np.ndarray:
     """RMS normalisation over the channel (last) axis with a per-channel gain:
     y = x / sqrt(mean(x**2) + eps) * gamma  [myzaker article, section on technical
@@ -156,6 +156,7 @@ def qk_norm_rope(x: np.ndarray, gamma, eps: float, grid, theta: float = 10000.0,
     return rope3d(rmsnorm(x, gamma, eps), grid, theta, token_offset)
 
 
+# --------------------------------------------------------------------------- layout
 def n_blocks_of(n_tokens: int) -> int:
     return -(-n_tokens // BLOCK)
 

@@ -9,6 +9,10 @@
  *       reads Q, K, V (bf16 bits, [1, HEADS, N, 64] each, N = T*H*W, in that order) from
  *       the file IN, runs lcv_bsa_build_layout and lcv_bsa_forward with the 3D-RoPE applied
  *       to Q and K (theta 1e4), and writes out (bf16 bits) and then lse (fp32) to OUT.
+ *   lcv_client cross_bwd_noquery HEADS KV_LEN
+ *       the cross-attention backward with no query (n_q = 0): every query-side pointer and
+ *       the workspace are NULL (its size is 0), dK and dV are filled with NaN bits first;
+ *       prints "zeros" if both come back as exact zeros.
  *
  * Every call's status is checked; on failure the library's message is printed and the
  * program exits with status 1.
@@ -120,12 +124,61 @@ static int forward(int argc, char** argv) {
   return 0;
 }
 
+static int cross_bwd_noquery(int argc, char** argv) {
+  if (argc != 4) return 2;
+  const int heads = atoi(argv[2]);
+  const int kv_len = atoi(argv[3]);
+  const size_t elems = (size_t)heads * (size_t)kv_len * LCV_HEAD_DIM;
+  const size_t bytes = elems * sizeof(uint16_t);
+  const int64_t ws = lcv_cross_attention_backward_workspace(1, heads, 0, kv_len);
+  if (ws != 0) {
+    fprintf(stderr, "workspace for n_q = 0 is %lld, expected 0\n", (long long)ws);
+    return 1;
+  }
+  uint16_t* host = (uint16_t*)malloc(bytes);
+  if (host == NULL) {
+    fprintf(stderr, "host allocation failed\n");
+    return 1;
+  }
+  for (size_t i = 0; i < elems; ++i) host[i] = (uint16_t)(0x3c00u + (i % 97u));   /* finite keys and values */
+  void *k, *v, *dk, *dv;
+  check_hip(hipMalloc(&k, bytes), "hipMalloc k");
+  check_hip(hipMalloc(&v, bytes), "hipMalloc v");
+  check_hip(hipMalloc(&dk, bytes), "hipMalloc dk");
+  check_hip(hipMalloc(&dv, bytes), "hipMalloc dv");
+  check_hip(hipMemcpy(k, host, bytes, hipMemcpyHostToDevice), "copy k");
+  check_hip(hipMemcpy(v, host, bytes, hipMemcpyHostToDevice), "copy v");
+  check_hip(hipMemset(dk, 0xff, bytes), "poison dk");
+  check_hip(hipMemset(dv, 0xff, bytes), "poison dv");
+  check_hip(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  check_lcv(lcv_cross_attention_backward(NULL, k, v, NULL, NULL, NULL, 1, heads, 0, kv_len, NULL, NULL, dk, dv, NULL,
+                                         0, 0),
+            "lcv_cross_attention_backward");
+  check_hip(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  int zeros = 1;
+  void* grads[2] = {dk, dv};
+  for (int t = 0; t < 2; ++t) {
+    check_hip(hipMemcpy(host, grads[t], bytes, hipMemcpyDeviceToHost), "copy gradient");
+    for (size_t i = 0; i < elems; ++i)
+      if (host[i] != 0) zeros = 0;
+  }
+  hipFree(k);
+  hipFree(v);
+  hipFree(dk);
+  hipFree(dv);
+  free(host);
+  printf("%s\n", zeros ? "zeros" : "nonzero");
+  return 0;
+}
+
 int main(int argc, char** argv) {
   int rc = 2;
   if (argc > 1 && strcmp(argv[1], "query") == 0) rc = query(argc, argv);
   if (argc > 1 && strcmp(argv[1], "forward") == 0) rc = forward(argc, argv);
+  if (argc > 1 && strcmp(argv[1], "cross_bwd_noquery") == 0) rc = cross_bwd_noquery(argc, argv);
   if (rc == 2)
     fprintf(stderr, "usage: lcv_client query N LOCAL STRIDE COND\n"
-                    "       lcv_client forward T H W HEADS LOCAL STRIDE COND IN OUT\n");
+                    "       lcv_client forward T H W HEADS LOCAL STRIDE COND IN OUT\n"
+                    "       lcv_client cross_bwd_noquery HEADS KV_LEN\n");
   return rc;
 }

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 8
+    assert bsa.lib().lcv_abi_version() == 9
 
 
 QUERY_CASES = [
@@ -122,9 +122,9 @@ def test_cross_attention_argument_errors():
 
 
 def _cross_bwd_workspace(batch, heads, n_q, kv_len):
-    """Expected scratch size: 2 values per query row (rounded up to 4), then fp32 partial dK
-    and dV per query chunk; chunks give about 512 key-walk workgroups, at most 64 and at most
-    one per query block, none empty."""
+    """Expected scratch size: 34 values per query row (the scaled Q as 64 bf16, lse and D;
+    rounded up to 4), then fp32 partial dK and dV per query chunk; chunks give about 512
+    key-walk workgroups, at most 64 and at most one per query block, none empty."""
     bh = batch * heads
     nqb, nkb = -(-n_q // 64), -(-kv_len // 64)
     groups = -(-nkb // 4)
@@ -133,7 +133,7 @@ def _cross_bwd_workspace(batch, heads, n_q, kv_len):
         chunks = min(-(-512 // (bh * groups)), 64, nqb)
         per = -(-nqb // chunks)
         chunks = -(-nqb // per)
-    return -(-2 * bh * n_q // 4) * 4 + 2 * chunks * bh * kv_len * 64
+    return -(-34 * bh * n_q // 4) * 4 + 2 * chunks * bh * kv_len * 64
 
 
 def test_cross_backward_workspace_sizes():
@@ -141,7 +141,7 @@ def test_cross_backward_workspace_sizes():
     for args in [(1, 1, 64, 64), (2, 3, 1000, 77), (1, 32, 58560, 512), (4, 2, 0, 512), (1, 1, 100, 0),
                  (3, 5, 4097, 300)]:
         assert f(*args) == _cross_bwd_workspace(*args), args
-    assert f(1, 1, 64, 64) == 128 + 2 * 64 * 64
+    assert f(1, 1, 64, 64) == 34 * 64 + 2 * 64 * 64
     assert f(0, 1, 64, 64) == -1 and f(1, 1, -1, 64) == -1 and f(1, 1, 64, -1) == -1
 
 
@@ -213,11 +213,21 @@ def test_backward_argument_errors():
     L = bsa.lib()
     p = ctypes.c_void_p(4096)
     f = L.lcv_bsa_backward
-    assert f(p, p, p, p, p, p, 1, 1, None, 0, p, p, p, p, None) == 1          # no layout
-    assert f(p, p, p, p, p, p, 1, 1, None, 0, p, p, p, None, None) == 1       # no workspace
-    assert f(p, p, p, p, None, p, 1, 1, None, 0, p, p, p, p, None) == 1       # no lse
-    assert f(p, p, p, p, p, None, 1, 1, None, 0, p, p, p, p, None) == 1       # no dout
+    big = 1 << 40
+    assert f(p, p, p, p, p, p, 1, 1, None, 0, p, p, p, p, big, None) == 1          # no layout
+    assert f(p, p, p, p, p, p, 1, 1, None, 0, p, p, p, None, big, None) == 1       # no workspace
+    assert f(p, p, p, p, None, p, 1, 1, None, 0, p, p, p, p, big, None) == 1       # no lse
+    assert f(p, p, p, p, p, None, 1, 1, None, 0, p, p, p, p, big, None) == 1       # no dout
     assert b"required" in L.lcv_last_error()
+
+
+def test_backward_workspace_sizes():
+    """136 bytes per query row: the scaled Q (64 bf16) and two fp32 per-row terms."""
+    f = bsa.lib().lcv_bsa_backward_workspace
+    assert f(1, 1, 64) == 34 * 64
+    assert f(1, 32, 86400) == 34 * 32 * 86400
+    assert f(2, 3, 631) == 34 * 6 * 631
+    assert f(0, 1, 64) == -1 and f(1, 0, 64) == -1 and f(1, 1, 0) == -1
 
 
 def test_rope_argument_errors():

@@ -3,7 +3,9 @@ include/lcv_bsa.h), outside the Python binding.
 
 CPU: the client's host-only calls (ABI version, layout closed form) against the oracle's CSR
 and attended-pair count.  GPU: the client's forward (layout build + RoPE-fused attention on
-device memory it allocates itself) against the oracle, with the forward's bounds."""
+device memory it allocates itself) against the oracle, with the forward's bounds; the
+cross-attention backward with no query and a NULL workspace of size 0, whose dK and dV
+must come back as zeros (the gradient of an attention that no query reads)."""
 from __future__ import annotations
 
 import subprocess
@@ -67,3 +69,13 @@ def test_c_client_forward(tmp_path):
                                       local, stride)
     assert_out_close(bf16_bits_to_f64(out), ref_o, "C client forward")
     assert_lse_close(lse.astype(np.float64), ref_l, "C client forward")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("heads,kv_len", [(2, 96), (3, 512)])
+def test_c_client_cross_backward_without_queries(heads, kv_len):
+    say(f"[c client] cross-attention backward, no query, heads {heads} text {kv_len}")
+    res = subprocess.run([_client(), "cross_bwd_noquery", str(heads), str(kv_len)], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "zeros", res.stdout

@@ -118,6 +118,72 @@ def test_backward_peaked_softmax(lib):
     layout.close()
 
 
+@pytest.mark.parametrize("offset", [3072.0, -3072.0], ids=["plus", "minus"])
+def test_backward_score_offset_far_from_zero(lib, offset):
+    """Every score of a row shifted by the same large amount (channel 0 of every key is 1, of
+    every query +-3072: +-384 in natural units).  The softmax ignores a shift common to its
+    row, so the gradients must match the oracle at the standard bounds.  The forward forms
+    that shift from Q * log2(e)/8 rounded to bf16 (an error of ~1.4 natural units in the
+    row's LSE); the backward recomputes P from the same rounded operand, so P = exp(S - lse)
+    stays a probability distribution.  A walk that scored with another rounding of the same
+    product (for instance K * log2(e)/8) would put a common factor of up to 2^3 on the row's
+    probabilities.  dK takes the rounded query too, which moves its channel 0 (the largest
+    gradient entries, 384 times the others) by at most 2^-8 relative."""
+    import torch
+    n, heads, cond, local, stride = 630, 2, 210, 2, 4
+    qb, kb, vb = qkv_bits(39, 1, heads, n)
+    gb = grad_bits(39, 1, heads, n)
+    qb, kb = qb.copy(), kb.copy()
+    qb[..., 0] = np.uint16(np.float32(offset).view(np.uint32) >> 16)      # +-3072 is exact in bf16
+    kb[..., 0] = np.uint16(np.float32(1.0).view(np.uint32) >> 16)
+    say(f"[bwd] score offset {offset:+.0f} on channel 0")
+    layout = lib.build_layout(n, local, stride, cond)
+    q, k, v, do = to_dev(qb), to_dev(kb), to_dev(vb), to_dev(gb)
+    out, lse = lib.forward(q, k, v, layout, grid=None)
+    dq, dk, dv = lib.backward(q, k, v, out, lse, do, layout)
+    _sync()
+    ref = oracle.bsa_backward(*(bf16_bits_to_f64(a) for a in (qb, kb, vb, gb)), cond, local, stride)
+    for what, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        _close(from_dev_f64(got), r, f"offset {offset:+.0f} {what}")
+    layout.close()
+
+
+def _gains(seed, lo, hi):
+    return np.random.default_rng(seed).uniform(lo, hi, 64)
+
+
+@pytest.mark.parametrize("glo,ghi", [(1.0, 2.0), (1.5, 2.5)], ids=["gains-1-2", "gains-1.5-2.5"])
+def test_backward_after_qk_norm_large_gains(lib, glo, ghi):
+    """Q and K through the QK prologue (RMSNorm with gains drawn from U(glo, ghi), then the
+    3D-RoPE) on the GPU, then the forward and backward on the normalised tensors, against the
+    oracle's backward of the same bf16 tensors.  Each channel of q and k is ~gain * N(0, 1),
+    so scores have a standard deviation of ~E[gain^2] natural units (2.3 and 4.1 here): rows
+    are peaked and many scores are large.  With the backward scoring from the forward's own
+    rounded Q the only score error left is that rounding (relative 2^-8 per product at most,
+    ~0.4 * 2^-8 in standard deviation), which moves each probability by ~0.17% * E[gain^2]
+    (0.4% and 0.7% in standard deviation): the standard bounds hold at these gains."""
+    import torch
+    grid = (3, 10, 21)
+    n, heads, cond, local, stride = 630, 2, 210, 2, 4
+    say(f"[bwd] after QK norm, gains U({glo}, {ghi})")
+    qb, kb, vb = qkv_bits(49, 1, heads, n)
+    gb = grad_bits(49, 1, heads, n)
+    gq = torch.from_numpy(_gains(5, glo, ghi).astype(np.float32)).cuda()
+    gk = torch.from_numpy(_gains(6, glo, ghi).astype(np.float32)).cuda()
+    layout = lib.build_layout(n, local, stride, cond)
+    q = lib.qk_rmsnorm_rope3d(to_dev(qb), gq, 1e-6, grid)
+    k = lib.qk_rmsnorm_rope3d(to_dev(kb), gk, 1e-6, grid)
+    v, do = to_dev(vb), to_dev(gb)
+    out, lse = lib.forward(q, k, v, layout, grid=None)
+    dq, dk, dv = lib.backward(q, k, v, out, lse, do, layout)
+    _sync()
+    qn, kn = from_dev_f64(q), from_dev_f64(k)
+    ref = oracle.bsa_backward(qn, kn, bf16_bits_to_f64(vb), bf16_bits_to_f64(gb), cond, local, stride)
+    for what, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        _close(from_dev_f64(got), r, f"gains U({glo}, {ghi}) {what}")
+    layout.close()
+
+
 def test_backward_writes_everything_and_is_deterministic(lib):
     """Gradients pre-filled with NaN come back finite; a second call gives identical bits."""
     import torch
@@ -125,7 +191,7 @@ def test_backward_writes_everything_and_is_deterministic(lib):
     n, heads = 630, 2
     _, (q, k, v, do, out, lse), (dq, dk, dv), layout = _run(lib, n, heads, 210, 2, 4, seed=42)
     poison = [torch.full_like(q, float("nan")) for _ in range(3)]
-    ws = torch.full((2 * heads * n,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((lib.backward_workspace(1, heads, n),), float("nan"), dtype=torch.float32, device="cuda")
     lib.backward(q, k, v, out, lse, do, layout, dq=poison[0], dk=poison[1], dv=poison[2], workspace=ws)
     _sync()
     for a, b in zip((dq, dk, dv), poison):
@@ -142,11 +208,16 @@ def test_backward_argument_errors(lib):
     p = ctypes.c_void_p(4096)
     f = L.lcv_bsa_backward
     h = layout.handle
-    assert f(p, p, p, p, p, p, 1, 2, h, 0, p, p, p, p, None) == 5                       # cond mismatch
-    assert f(p, p, p, p, p, p, 0, 2, h, 210, p, p, p, p, None) == 2                     # batch 0
-    assert f(p, p, p, p, p, p, 1, 0, h, 210, p, p, p, p, None) == 2                     # heads 0
-    assert f(ctypes.c_void_p(4104), p, p, p, p, p, 1, 2, h, 210, p, p, p, p, None) == 2  # misaligned q
-    assert f(p, p, p, p, ctypes.c_void_p(4098), p, 1, 2, h, 210, p, p, p, p, None) == 2  # misaligned lse
+    big = 1 << 40
+    need = L.lcv_bsa_backward_workspace(1, 2, 630)
+    assert f(p, p, p, p, p, p, 1, 2, h, 0, p, p, p, p, big, None) == 5                       # cond mismatch
+    assert f(p, p, p, p, p, p, 0, 2, h, 210, p, p, p, p, big, None) == 2                     # batch 0
+    assert f(p, p, p, p, p, p, 1, 0, h, 210, p, p, p, p, big, None) == 2                     # heads 0
+    assert f(ctypes.c_void_p(4104), p, p, p, p, p, 1, 2, h, 210, p, p, p, p, big, None) == 2  # misaligned q
+    assert f(p, p, p, p, ctypes.c_void_p(4098), p, 1, 2, h, 210, p, p, p, p, big, None) == 2  # misaligned lse
+    assert f(p, p, p, p, p, p, 1, 2, h, 210, p, p, p, ctypes.c_void_p(4100), big, None) == 2  # workspace not 16-aligned
+    assert f(p, p, p, p, p, p, 1, 2, h, 210, p, p, p, p, need - 1, None) == 2                # workspace too small
+    assert b"workspace" in L.lcv_last_error()
     layout.close()
 
 

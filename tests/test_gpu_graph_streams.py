@@ -48,7 +48,7 @@ class Chain:
         self.lse = torch.empty((1, HEADS, N), dtype=torch.float32, device="cuda")
         self.xlse = torch.empty_like(self.lse)
         self.dgq, self.dgk = (torch.empty(64, dtype=torch.float32, device="cuda") for _ in range(2))
-        self.ws = torch.empty(2 * HEADS * N, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(lib.backward_workspace(1, HEADS, N), dtype=torch.float32, device="cuda")
         self.pws = torch.empty(lib.lib().lcv_qk_rmsnorm_rope3d_backward_workspace(HEADS, N), dtype=torch.float32,
                                device="cuda")
         self.xws = torch.empty(lib.cross_attention_backward_workspace(1, HEADS, N, 96), dtype=torch.float32,
