@@ -320,6 +320,55 @@ CrossBwdPlan cross_bwd_plan(int64_t bh, int32_t n_q, int32_t kv_len) {
   return pl;
 }
 
+// Shared checks and launch of the two prologue backward entry points: the caller's workspace,
+// or (static_scratch) the library's static scratch array of the current device, looked up
+// after every check has passed.
+lcv_status prologue_bwd_common(const void* x, const void* dy, const float* gamma, float eps, int64_t n_outer,
+                               int32_t n_tokens, int32_t token_offset, const lcv_rope3d_grid* grid, void* dx,
+                               float* dgamma, float* workspace, int64_t workspace_floats, bool static_scratch,
+                               hipStream_t stream) {
+  if (x == nullptr || dy == nullptr || gamma == nullptr || dx == nullptr || dgamma == nullptr)
+    return fail(LCV_ERR_NULL, "x, dy, gamma, dx and dgamma are required");
+  if (n_outer < 0 || n_tokens < 0 || token_offset < 0)
+    return fail(LCV_ERR_INVALID_ARG, "n_outer, n_tokens and token_offset must be >= 0");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(LCV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16))
+    return fail(LCV_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
+  if (!aligned(gamma, 16) || !aligned(dgamma, 4) || !aligned(workspace, 4))
+    return fail(LCV_ERR_INVALID_ARG, "gamma must be 16-byte aligned, dgamma and workspace 4-byte aligned");
+  if (grid != nullptr) {
+    lcv_status st = check_grid(grid);
+    if (st != LCV_OK) return st;
+    const int64_t total = (int64_t)grid->T * grid->H * grid->W;
+    if ((int64_t)token_offset + n_tokens > total)
+      return fail(LCV_ERR_SHAPE, "tokens [%d, %lld) exceed the grid's %lld tokens", token_offset,
+                  (long long)token_offset + n_tokens, (long long)total);
+  } else if ((int64_t)token_offset + n_tokens >= (int64_t(1) << 31)) {
+    return fail(LCV_ERR_UNSUPPORTED, "token_offset + n_tokens must be below 2^31");
+  }
+  if (n_outer > (int64_t)65535 * lcv::kPrologueBwdSlices)
+    return fail(LCV_ERR_UNSUPPORTED, "n_outer above %lld is not supported", (long long)65535 * lcv::kPrologueBwdSlices);
+  const int64_t need = lcv::prologue_bwd_workspace_floats(n_outer, n_tokens);
+  if (static_scratch) {
+    if (need > lcv::kNoAllocPartialFloats)
+      return fail(LCV_ERR_UNSUPPORTED,
+                  "n_outer %lld x n_tokens %d needs %lld scratch values; the static scratch holds %lld "
+                  "(use lcv_qk_rmsnorm_rope3d_backward with a workspace)",
+                  (long long)n_outer, n_tokens, (long long)need, (long long)lcv::kNoAllocPartialFloats);
+    const hipError_t se = lcv::prologue_bwd_scratch(&workspace);
+    if (se != hipSuccess) return hip_fail(se, "static scratch of the prologue backward");
+  } else if (workspace_floats < need) {
+    return fail(LCV_ERR_INVALID_ARG, "workspace holds %lld floats, %lld needed", (long long)workspace_floats,
+                (long long)need);
+  }
+  const hipError_t e = lcv::launch_qk_prologue_bwd(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), gamma, eps, n_outer, n_tokens, token_offset,
+      grid != nullptr, grid ? grid->H : 1, grid ? grid->W : 1, grid ? std::log2(grid->theta) : 0.f,
+      static_cast<uint16_t*>(dx), dgamma, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "qk prologue backward launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -495,37 +544,17 @@ lcv_status lcv_qk_rmsnorm_rope3d_backward(const void* x, const void* dy, const f
                                           int64_t n_outer, int32_t n_tokens, int32_t token_offset,
                                           const lcv_rope3d_grid* grid, void* dx, float* dgamma, float* workspace,
                                           int64_t workspace_floats, hipStream_t stream) {
-  if (x == nullptr || dy == nullptr || gamma == nullptr || dx == nullptr || dgamma == nullptr || workspace == nullptr)
-    return fail(LCV_ERR_NULL, "x, dy, gamma, dx, dgamma and workspace are required");
-  if (n_outer < 0 || n_tokens < 0 || token_offset < 0)
-    return fail(LCV_ERR_INVALID_ARG, "n_outer, n_tokens and token_offset must be >= 0");
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(LCV_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16))
-    return fail(LCV_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
-  if (!aligned(gamma, 16) || !aligned(dgamma, 4) || !aligned(workspace, 4))
-    return fail(LCV_ERR_INVALID_ARG, "gamma must be 16-byte aligned, dgamma and workspace 4-byte aligned");
-  if (grid != nullptr) {
-    lcv_status st = check_grid(grid);
-    if (st != LCV_OK) return st;
-    const int64_t total = (int64_t)grid->T * grid->H * grid->W;
-    if ((int64_t)token_offset + n_tokens > total)
-      return fail(LCV_ERR_SHAPE, "tokens [%d, %lld) exceed the grid's %lld tokens", token_offset,
-                  (long long)token_offset + n_tokens, (long long)total);
-  } else if ((int64_t)token_offset + n_tokens >= (int64_t(1) << 31)) {
-    return fail(LCV_ERR_UNSUPPORTED, "token_offset + n_tokens must be below 2^31");
-  }
-  if (n_outer > (int64_t)65535 * lcv::kPrologueBwdSlices)
-    return fail(LCV_ERR_UNSUPPORTED, "n_outer above %lld is not supported", (long long)65535 * lcv::kPrologueBwdSlices);
-  const int64_t need = lcv::prologue_bwd_workspace_floats(n_outer, n_tokens);
-  if (workspace_floats < need)
-    return fail(LCV_ERR_INVALID_ARG, "workspace holds %lld floats, %lld needed", (long long)workspace_floats,
-                (long long)need);
-  const hipError_t e = lcv::launch_qk_prologue_bwd(
-      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), gamma, eps, n_outer, n_tokens, token_offset,
-      grid != nullptr, grid ? grid->H : 1, grid ? grid->W : 1, grid ? std::log2(grid->theta) : 0.f,
-      static_cast<uint16_t*>(dx), dgamma, workspace, stream);
-  if (e != hipSuccess) return hip_fail(e, "qk prologue backward launch");
-  return ok();
+  if (workspace == nullptr) return fail(LCV_ERR_NULL, "workspace is required");
+  return prologue_bwd_common(x, dy, gamma, eps, n_outer, n_tokens, token_offset, grid, dx, dgamma, workspace,
+                             workspace_floats, false, stream);
+}
+
+lcv_status lcv_qk_rmsnorm_rope3d_backward_noalloc(const void* x, const void* dy, const float* gamma, float eps,
+                                                  int64_t n_outer, int32_t n_tokens, int32_t token_offset,
+                                                  const lcv_rope3d_grid* grid, void* dx, float* dgamma,
+                                                  hipStream_t stream) {
+  return prologue_bwd_common(x, dy, gamma, eps, n_outer, n_tokens, token_offset, grid, dx, dgamma, nullptr, 0, true,
+                             stream);
 }
 
 lcv_status lcv_attn_merge(const void* const* outs, const float* const* lses, int32_t n_parts, int64_t rows,

@@ -27,6 +27,14 @@ inline int64_t prologue_bwd_workspace_floats(int64_t n_outer, int32_t n_tokens) 
   return g.x * g.y * 64;
 }
 
+// The allocation-free entry point keeps the workgroups' partials in a static device array of
+// this many floats (4 MiB: 16,384 workgroup partials, e.g. 512 (batch, head) slices of up to
+// 16,384 tokens each, or 32 slices of any length).
+constexpr int64_t kNoAllocPartialFloats = int64_t(1) << 20;
+
+// Address of that array on the current device, looked up once per device.
+hipError_t prologue_bwd_scratch(float** ptr);
+
 hipError_t launch_qk_prologue_bwd(const uint16_t* x, const uint16_t* dy, const float* gamma, float eps, int64_t n_outer,
                                   int32_t n_tokens, int32_t token_offset, bool rope, int32_t H, int32_t W,
                                   float log2_theta, uint16_t* dx, float* dgamma, float* partials, hipStream_t stream);

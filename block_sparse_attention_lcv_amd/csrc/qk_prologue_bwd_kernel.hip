@@ -12,6 +12,8 @@
 // per iteration with all four 16-byte loads in flight.  Each workgroup writes its 64 partial
 // sums of dgamma to the workspace; a second kernel adds them in a fixed order, so the result
 // is deterministic.
+#include <mutex>
+
 #include "prologue_bwd.h"
 #include "rope_math.h"
 
@@ -196,7 +198,35 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(const float* partial
   }
 }
 
+// Scratch of lcv_qk_rmsnorm_rope3d_backward_noalloc: the workgroups' dgamma partials, for
+// callers that cannot allocate.  The loader gives every GPU the library runs on its own copy
+// with the code object (held until the process ends); in host code the name is only a handle
+// for hipGetSymbolAddress, never a device address.  Calls on one GPU share it: overlapping
+// calls race.  Every workgroup writes its own partial before the sum kernel reads it, so no
+// call needs it cleared.
+static __device__ __align__(256) float scratch[kNoAllocPartialFloats];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices] = {};
+
 }  // namespace
+
+hipError_t prologue_bwd_scratch(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_qk_prologue_bwd(const uint16_t* x, const uint16_t* dy, const float* gamma, float eps, int64_t n_outer,
                                   int32_t n_tokens, int32_t token_offset, bool rope, int32_t H, int32_t W,

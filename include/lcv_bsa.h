@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 9
+#define LCV_BSA_ABI_VERSION 10
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -215,6 +215,21 @@ lcv_status lcv_qk_rmsnorm_rope3d_backward(const void* x, const void* dy, const f
                                           int64_t n_outer, int32_t n_tokens, int32_t token_offset,
                                           const lcv_rope3d_grid* grid, void* dx, float* dgamma, float* workspace,
                                           int64_t workspace_floats, hipStream_t stream);
+
+/* lcv_qk_rmsnorm_rope3d_backward without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The dgamma partials go to a static
+ * device array of the library (4 MiB, 1,048,576 fp32 values: one 64-value partial per
+ * workgroup, i.e. sizes with lcv_qk_rmsnorm_rope3d_backward_workspace(n_outer, n_tokens) <=
+ * 1,048,576), of which every GPU the library runs on holds its own copy until the process
+ * ends.  Every call on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  Same arguments,
+ * results (bitwise) and errors as lcv_qk_rmsnorm_rope3d_backward, plus UNSUPPORTED for sizes
+ * beyond the array. */
+lcv_status lcv_qk_rmsnorm_rope3d_backward_noalloc(const void* x, const void* dy, const float* gamma, float eps,
+                                                  int64_t n_outer, int32_t n_tokens, int32_t token_offset,
+                                                  const lcv_rope3d_grid* grid, void* dx, float* dgamma,
+                                                  hipStream_t stream);
 
 /* Backward of lcv_bsa_forward (flags = 0): the gradients of the attention for the upstream
  * gradient dout, for training (myzaker article, technical principles: the LoRA-trained

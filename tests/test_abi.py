@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 9
+    assert bsa.lib().lcv_abi_version() == 10
 
 
 QUERY_CASES = [
