@@ -88,11 +88,33 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 raw, int c, const Coords& xyz,
 // Staging of K/V block j into an LDS stage.  The 8 KB tile is moved as 8 wave-loads of
 // 1 KB (8 rows); wavefront w issues loads u = w*kLoadsPerWave + c.  In load u, lane l carries
 // row 8u + l/8 and lands at LDS byte 1024u + 16l, i.e. physical chunk l%8 of that row, which
-// holds logical chunk (l%8) ^ swz(8u + l/8) under the swizzle of tile_off.  Rows past the end
-// of the sequence read row N-1 (finite data; their scores are masked and their
-// probabilities are zero).
+// holds logical chunk (l%8) ^ swz(8u + l/8) under the swizzle of tile_off.  The copies are
+// buffer loads straight into LDS: the block's first row is the (wave-uniform) base of a
+// buffer resource built with scalar instructions, each lane's byte offset inside the block
+// is fixed for the whole walk (computed once), and the resource's size stops at the end of
+// the keys, so rows past it read zeros (their scores are masked and their probabilities are
+// zero).  The vector ALU computes no address per copy.
 constexpr int kLoadsPerWave = 8 / kWaves;
 static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
+
+typedef __attribute__((address_space(4))) const int32_t const_i32;   // scalar loads of the lists
+
+// Raw buffer resource (no stride, 32-bit data format) over `rows` key rows of 128 bytes from
+// the byte address `base`; both wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(uint64_t base, int rows) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const int bytes = __builtin_amdgcn_readfirstlane(rows * 128);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
+}
+
+// Lane offset (bytes) of load c inside a K or V block: row 8u + l/8, physical chunk l%8
+// holding logical chunk (l%8) ^ swz(row).
+__device__ __forceinline__ uint32_t stage_lane_offset(int wave, int lane, int c) {
+  const int u = wave * kLoadsPerWave + c;
+  const int row = 8 * u + (lane >> 3);
+  return (uint32_t)(row * 128 + 16 * ((lane & 7) ^ swz(row)));
+}
 
 // Where the rows of one (batch, head)'s keys and values live, as byte addresses of key row 0
 // (wave-uniform, computed once): key row `key` is at cond + 128 key when key < split (the
@@ -102,7 +124,8 @@ static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
 struct KvSrc {
   uint64_t k_cond, v_cond, k_noise, v_noise;
   int split;      // 0 unless cached
-  int key_end;    // keys [0, key_end) exist; rows past it read the last one
+  int key_end;    // keys [0, key_end) exist; rows past it read zeros (the K rows rotated in
+                  // the kernel: the last row)
 };
 
 template <bool CACHED, bool CROSS>
@@ -135,24 +158,54 @@ __device__ __forceinline__ const uint16_t* kv_row(const KvSrc& s, bool is_k, int
   return reinterpret_cast<const uint16_t*>(base + (uint64_t)key * 128 + 16 * chunk);
 }
 
-// Issue the asynchronous global -> LDS copies of block j into a stage's K and V tiles (V
-// always, K too unless K is rotated on the way); K chunks to be rotated are loaded into kreg.
+// Issue the asynchronous copies of block j into a stage's K and V tiles (V always, K too
+// unless K is rotated on the way); K chunks to be rotated are loaded into kreg.  In the cached
+// call a block lies in the condition cache, in the noise tensor, or (the block holding the
+// boundary) in both: then each source is copied by the lanes whose rows it holds.
 template <bool ROPE_K, bool CACHED>
 __device__ __forceinline__ void stage_issue(const KvSrc& src, unsigned char* kdst, unsigned char* vdst, int j, int wave,
-                                            int lane, u32x4 (&kreg)[kLoadsPerWave]) {
+                                            int lane, const uint32_t (&voff)[kLoadsPerWave],
+                                            u32x4 (&kreg)[kLoadsPerWave]) {
+  const int row0 = 64 * j;
+  // copies from the tensors whose key row 0 is at kbase / vbase, rows below `limit`, by the
+  // lanes for which on(c) holds
+  auto issue = [&](uint64_t kbase, uint64_t vbase, int limit, auto&& on) __attribute__((always_inline)) {
+    int rows = limit - row0;
+    rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + (uint64_t)row0 * 128, rows);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + (uint64_t)row0 * 128, rows);
 #pragma unroll
-  for (int c = 0; c < kLoadsPerWave; ++c) {
-    const int u = wave * kLoadsPerWave + c;
-    const int gch = (lane & 7) ^ swz(8 * u + (lane >> 3));
-    const int key = 64 * j + 8 * u + (lane >> 3);
-    const int row0 = 64 * j + 8 * u;
-    const uint16_t* vsrc = kv_row<CACHED>(src, false, row0, key, gch);
-    __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + 1024 * u), 16, 0, 0);
-    const uint16_t* ksrc = kv_row<CACHED>(src, true, row0, key, gch);
-    if constexpr (ROPE_K)
-      kreg[c] = *reinterpret_cast<const u32x4*>(ksrc);
-    else
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + 1024 * u), 16, 0, 0);
+    for (int c = 0; c < kLoadsPerWave; ++c) {
+      const int u = wave * kLoadsPerWave + c;
+      if (on(c)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + 1024 * u), 16, voff[c], 0, 0, 0);
+        if constexpr (!ROPE_K)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + 1024 * u), 16, voff[c], 0, 0, 0);
+      }
+    }
+  };
+  auto all = [](int) { return true; };
+  if constexpr (!CACHED) {
+    issue(src.k_noise, src.v_noise, src.key_end, all);
+  } else {
+    if (row0 + 64 <= src.split) {
+      issue(src.k_cond, src.v_cond, src.split, all);
+    } else if (row0 >= src.split) {
+      issue(src.k_noise, src.v_noise, src.key_end, all);
+    } else {
+      auto key = [&](int c) { return row0 + 8 * (wave * kLoadsPerWave + c) + (lane >> 3); };
+      issue(src.k_cond, src.v_cond, src.split, [&](int c) { return key(c) < src.split; });
+      issue(src.k_noise, src.v_noise, src.key_end, [&](int c) { return key(c) >= src.split; });
+    }
+  }
+  if constexpr (ROPE_K) {
+#pragma unroll
+    for (int c = 0; c < kLoadsPerWave; ++c) {
+      const int u = wave * kLoadsPerWave + c;
+      const int gch = (lane & 7) ^ swz(8 * u + (lane >> 3));
+      const int key = row0 + 8 * u + (lane >> 3);
+      kreg[c] = *reinterpret_cast<const u32x4*>(kv_row<CACHED>(src, true, row0 + 8 * u, key, gch));
+    }
   }
 }
 
@@ -316,24 +369,27 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 
   // the workgroup's list: layout-built (self-attention), or every text block for all four
   // wavefronts (cross-attention)
-  const int32_t* ents = CROSS ? nullptr : P.st_ent + P.row_ptr[st * kWaves];
+  const const_i32* ents = CROSS ? nullptr : (const const_i32*)P.st_ent + P.row_ptr[st * kWaves];
   const int cnt = CROSS ? (key_end + 63) >> 6 : P.st_cnt[st];
   auto entry = [&](int e) __attribute__((always_inline)) {
     if constexpr (CROSS)
       return (e << 8) | ((1 << kWaves) - 1);
     else
-      return ents[e];
+      return (int)ents[e];
   };
 
-  // List entries are wave-uniform (SGPRs): entry e+1 is known when step e starts (its block
-  // is copied during step e) and entry e+2 is loaded during step e.
+  // List entries are wave-uniform (SGPRs, scalar loads): entry e+1 is known when step e
+  // starts (its block is copied during step e) and entry e+2 is loaded during step e.
   u32x4 kreg[kLoadsPerWave];
+  uint32_t voff[kLoadsPerWave];
+#pragma unroll
+  for (int c = 0; c < kLoadsPerWave; ++c) voff[c] = stage_lane_offset(wave, lane, c);
   int ent_cur = 0, ent_next = 0;
   if (cnt > 0) {
     ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
     if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
     const int j0 = ent_cur >> 8;
-    stage_issue<ROPE_K, CACHED>(kvs, lds_k0, lds_v0, j0, wave, lane, kreg);
+    stage_issue<ROPE_K, CACHED>(kvs, lds_k0, lds_v0, j0, wave, lane, voff, kreg);
     if constexpr (ROPE_K) stage_store_k(P, lds_k0, j0, wave, lane, tab, kreg);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -361,7 +417,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   // scores relative to the rows' current references (nothing to do while every row of the
   // wavefront keeps the reference 0, or has none yet)
   auto rebase = [&](f32x16 (&s)[2]) {
-    if (ref_nonzero) {
+    if (__builtin_expect(ref_nonzero, 0)) {
       const float f0 = (mref[0] == -INFINITY) ? 0.f : mref[0];
       const float f1 = (mref[1] == -INFINITY) ? 0.f : mref[1];
 #pragma unroll
@@ -477,7 +533,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
     }
-    if (__any(trig[0] || trig[1])) softmax_slow(s0, p0, psum, trig, delta);
+    if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s0, p0, psum, trig, delta);
     lsum[0] += psum[0];
     lsum[1] += psum[1];
     if (MASK) mask_half(key0, 1, s1);
@@ -492,7 +548,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
     }
-    if (__any(trig[0] || trig[1])) softmax_slow(s1, p1, psum, trig, delta);
+    if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s1, p1, psum, trig, delta);
     lsum[0] += psum[0];
     lsum[1] += psum[1];
     pv_half(stage_tag, 1, p1);
@@ -505,7 +561,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     // copies of block e+1 into the other stage; past the end of the list they re-read block
     // 0 into that stage, which nothing reads any more
     auto copies = [&]() __attribute__((always_inline)) {
-      stage_issue<ROPE_K, CACHED>(kvs, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, jn, wave, lane, kreg);
+      stage_issue<ROPE_K, CACHED>(kvs, STAGE ? lds_k0 : lds_k1, STAGE ? lds_v0 : lds_v1, jn, wave, lane, voff, kreg);
     };
     // in flight until the barrier below (all lanes load the same entry)
     const int ent_after_raw = (e + 2 < cnt) ? entry(e + 2) : 0;
@@ -516,7 +572,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       // same in every variant because the register allocation of the cached one spilled
       // inside the loop without it)
       const bool need_mask = 64 * j + 63 >= key_end || (64 * qblk < P.C && 64 * j + 63 >= P.C);
-      if (need_mask)
+      if (__builtin_expect(need_mask, 0))
         attend(stage_tag, std::true_type{}, j, copies);
       else
         attend(stage_tag, std::false_type{}, j, copies);
