@@ -277,24 +277,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- work item: XCD x (= blockIdx % 8) takes the x-th contiguous slice of items
-  const int per_xcd = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= P.n_items) return;
-  const int bh = item / P.n_st_active;
-  const int st = P.st_first + (item - bh * P.n_st_active);
-  // keys [0, key_end) exist: the sequence (self-attention) or the batch item's text length
-  int key_end = P.N;
-  if constexpr (CROSS) {
-    key_end = P.kv_len;
-    if (P.kv_lens != nullptr) {
-      const int len = P.kv_lens[bh / P.heads];
-      key_end = len < 0 ? 0 : (len < P.kv_len ? len : P.kv_len);
-    }
-    key_end = __builtin_amdgcn_readfirstlane(key_end);
-  }
-  const KvSrc kvs = kv_src<CACHED, CROSS>(P, bh, key_end);
-
   // ---- cos/sin table of every (axis, position, pair) of the grid
   float2* tab = reinterpret_cast<float2*>(smem);
   if constexpr (ROPE_Q || ROPE_K) {
@@ -313,6 +295,30 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     }
     __syncthreads();
   }
+
+  // ---- work item (a (batch, head) and a workgroup list of 4 query blocks): XCD x (=
+  // blockIdx % 8) runs the x-th contiguous eighth of the items, head after head, so that the
+  // key blocks its workgroups share stay in its L2; inside a head the lists come in the
+  // layout's work order (longest first, in runs of consecutive lists).  The hardware starts
+  // each workgroup as a slot frees up, so the longest lists of a head go first and the
+  // shortest fill the end.
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= P.n_items) return;
+  const int bh = item / P.n_st_active;
+  const int level = item - bh * P.n_st_active;
+  const int st = P.st_order != nullptr ? P.st_order[level] : P.st_first + level;
+  // keys [0, key_end) exist: the sequence (self-attention) or the batch item's text length
+  int key_end = P.N;
+  if constexpr (CROSS) {
+    key_end = P.kv_len;
+    if (P.kv_lens != nullptr) {
+      const int len = P.kv_lens[bh / P.heads];
+      key_end = len < 0 ? 0 : (len < P.kv_len ? len : P.kv_len);
+    }
+    key_end = __builtin_amdgcn_readfirstlane(key_end);
+  }
+  const KvSrc kvs = kv_src<CACHED, CROSS>(P, bh, key_end);
 
   // ---- this wavefront's query block as MFMA B operands: qf[qt][ks] holds rows
   // 32*qt + (lane & 31), channels 16*ks + 8*(lane >> 5) .. +7, scaled by log2(e)/8
@@ -626,9 +632,11 @@ hipError_t launch_variant(const FwdParams& p, unsigned groups, size_t lds, hipSt
 
 }  // namespace
 
+unsigned item_groups(int64_t n_items) { return (unsigned)((n_items + 7) / 8 * 8); }
+
 hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.n_items == 0) return hipSuccess;
-  const unsigned groups = (unsigned)(((int64_t)p.n_items + 7) / 8 * 8);
+  const unsigned groups = item_groups(p.n_items);
   const bool rq = (p.flags & LCV_ROPE_Q) != 0, rk = (p.flags & LCV_ROPE_K) != 0, cached = p.kv_split > 0;
   const size_t lds = (rq || rk) ? (size_t)p.rope_entries * sizeof(float2) : 0;
   const int v = (rq ? 4 : 0) | (rk ? 2 : 0) | (cached ? 1 : 0);
@@ -646,7 +654,7 @@ hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_cross_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.n_items == 0) return hipSuccess;
-  const unsigned groups = (unsigned)(((int64_t)p.n_items + 7) / 8 * 8);
+  const unsigned groups = item_groups(p.n_items);
   return launch_variant<false, false, false, true>(p, groups, 0, stream);
 }
 

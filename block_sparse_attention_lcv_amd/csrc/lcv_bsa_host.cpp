@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -251,6 +252,10 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
   p.st_first = st_first;
   p.n_st_active = st_end - st_first;
   p.n_items = (int32_t)n_items;
+  p.bh_count = (int32_t)bh;
+  // the lists by decreasing length when the call covers every query row; a row range or the
+  // cached call walks its lists in order
+  p.st_order = (q_row0 == 0 && q_end == N) ? layout->dev.st_order : nullptr;
   p.flags = flags;
   if (flags) {
     p.T = grid->T;
@@ -433,6 +438,26 @@ lcv_status lcv_bsa_build_layout(const lcv_bsa_layout_params* params, hipStream_t
     lcv_bsa_layout_destroy(h);
     return fail(LCV_ERR_HIP, "layout build produced %d entries, expected %lld", gpu_nnz, (long long)info.nnz);
   }
+  // the forward's work order: the workgroup lists by decreasing length in 16 classes of
+  // length (class c holds lengths in [c, c+1) * max / 16), in index order inside a class, so
+  // that neighbouring lists (which share local key blocks) stay together
+  {
+    std::vector<int32_t> cnt(h->dev.n_st), order(h->dev.n_st);
+    e = hipMemcpy(cnt.data(), h->dev.st_cnt, cnt.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+    int64_t cmax = 1;
+    for (int32_t c : cnt) cmax = c > cmax ? c : cmax;
+    auto cls = [&](int32_t i) { return (int64_t)cnt[i] * 16 / (cmax + 1); };
+    for (int32_t i = 0; i < h->dev.n_st; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cls(a) > cls(b); });
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&h->dev.st_order), order.size() * sizeof(int32_t));
+    if (e == hipSuccess)
+      e = hipMemcpy(h->dev.st_order, order.data(), order.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      lcv_bsa_layout_destroy(h);
+      return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "work order of the layout: %s",
+                  hipGetErrorString(e));
+    }
+  }
   // key-side schedule of the backward
   const KeyGroups kg = build_key_groups(L);
   h->dev.n_kg = (int32_t)kg.cnt.size();
@@ -482,6 +507,7 @@ void lcv_bsa_layout_destroy(lcv_bsa_layout* layout) {
   (void)hipFree(layout->dev.col_idx);
   (void)hipFree(layout->dev.st_cnt);
   (void)hipFree(layout->dev.st_ent);
+  (void)hipFree(layout->dev.st_order);
   (void)hipFree(layout->dev.kg_blk);
   (void)hipFree(layout->dev.kg_cnt);
   (void)hipFree(layout->dev.kg_off);
@@ -620,6 +646,8 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
   p.st_first = 0;
   p.n_st_active = n_st;
   p.n_items = (int32_t)n_items;
+  p.bh_count = (int32_t)bh;
+  p.st_order = nullptr;   // every list is the whole text: equal lengths
   p.flags = 0;
   p.kv_len = kv_len;
   p.kv_lens = kv_lens;

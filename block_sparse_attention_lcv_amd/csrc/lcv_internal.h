@@ -119,6 +119,7 @@ struct LayoutDev {
   int32_t* col_idx;   // [nnz]
   int32_t* st_cnt;    // [n_st] entries of each workgroup's key-block list
   int32_t* st_ent;    // [nnz]   list of workgroup st starts at row_ptr[st*kWaves]: (j << 8) | wave mask
+  int32_t* st_order;  // [n_st]  the forward's work order: lists by decreasing length class, index order inside
   int32_t n_st;       // ceil(n / kWaves)
   // Key-side schedule of the backward (column walk): key blocks in groups of kWaves whose
   // columns (attending query blocks) are nearly the same -- the strided global blocks
@@ -151,6 +152,9 @@ struct FwdParams {
   int32_t st_first;         // first workgroup list used
   int32_t n_st_active;      // workgroup lists per (batch, head)
   int32_t n_items;          // BH * n_st_active
+  int32_t bh_count;         // BH (batch * heads)
+  const int32_t* st_order;  // [n_st] the layout's work order of the lists (full calls), or nullptr:
+                            // lists st_first, st_first + 1, ... in order
   uint32_t flags;
   int32_t T, H, W;
   FastDiv div_hw, div_w;
