@@ -106,54 +106,6 @@ lcv_status compute_info(const lcv_bsa_layout_params* p, lcv_bsa_layout_info* inf
   return LCV_OK;
 }
 
-// Key-side schedule of the backward (column walk), built on the host from the row rule:
-// the columns of the CSR, key blocks grouped kWaves at a time (the strided global blocks,
-// whose columns are nearly all rows, together; the others in ascending runs), and per group
-// the ascending union of its columns with a per-slot membership mask.
-struct KeyGroups {
-  std::vector<int32_t> blk, cnt, off, ent;
-};
-
-KeyGroups build_key_groups(const lcv::LayoutRule& L) {
-  std::vector<std::vector<int32_t>> col(L.n);
-  for (int32_t i = 0; i < L.n; ++i) {
-    const lcv::RowShape rs = lcv::row_shape(L, i);
-    for (int32_t r = 0; r < rs.len; ++r) col[lcv::row_elem(L, rs, r)].push_back(i);
-  }
-  std::vector<int32_t> order;
-  order.reserve(L.n);
-  for (int32_t j = 0; j < L.n; ++j)
-    if (L.s > 0 && j % L.s == 0) order.push_back(j);
-  for (int32_t j = 0; j < L.n; ++j)
-    if (!(L.s > 0 && j % L.s == 0)) order.push_back(j);
-  KeyGroups kg;
-  std::vector<int32_t> mask(L.n, 0);
-  for (size_t g0 = 0; g0 < order.size(); g0 += lcv::kWaves) {
-    int32_t lo = L.n, hi = -1;
-    for (int b = 0; b < lcv::kWaves; ++b) {
-      const size_t idx = g0 + b;
-      const int32_t j = idx < order.size() ? order[idx] : -1;
-      kg.blk.push_back(j);
-      if (j < 0) continue;
-      for (int32_t i : col[j]) {
-        mask[i] |= 1 << b;
-        lo = i < lo ? i : lo;
-        hi = i > hi ? i : hi;
-      }
-    }
-    kg.off.push_back((int32_t)kg.ent.size());
-    int32_t c = 0;
-    for (int32_t i = lo; i <= hi; ++i)
-      if (mask[i] != 0) {
-        kg.ent.push_back((i << 8) | mask[i]);
-        mask[i] = 0;
-        ++c;
-      }
-    kg.cnt.push_back(c);
-  }
-  return kg;
-}
-
 lcv_status check_grid(const lcv_rope3d_grid* grid) {
   if (grid == nullptr) return fail(LCV_ERR_NULL, "grid is NULL");
   if (grid->T < 1 || grid->H < 1 || grid->W < 1)
@@ -411,72 +363,45 @@ lcv_status lcv_bsa_build_layout(const lcv_bsa_layout_params* params, hipStream_t
   }
   const int32_t n = info.n_blocks;
   h->dev.n_st = (n + lcv::kWaves - 1) / lcv::kWaves;
+  h->dev.n_kg = (n + lcv::kWaves - 1) / lcv::kWaves;
+  // one device allocation, carved into 256-byte aligned arrays
   const size_t nnz_alloc = info.nnz > 0 ? (size_t)info.nnz : 1;
   struct {
     int32_t** p;
     size_t count;
-  } bufs[] = {{&h->dev.row_ptr, (size_t)n + 1}, {&h->dev.col_idx, nnz_alloc},
-              {&h->dev.st_cnt, (size_t)h->dev.n_st}, {&h->dev.st_ent, nnz_alloc}};
-  for (auto& b : bufs) {
-    e = hipMalloc(reinterpret_cast<void**>(b.p), b.count * sizeof(int32_t));
-    if (e != hipSuccess) {
-      lcv_bsa_layout_destroy(h);
-      return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "hipMalloc of the layout: %s",
-                  hipGetErrorString(e));
-    }
+  } parts[] = {{&h->dev.row_ptr, (size_t)n + 1},         {&h->dev.col_idx, nnz_alloc},
+               {&h->dev.st_cnt, (size_t)h->dev.n_st},    {&h->dev.st_ent, nnz_alloc},
+               {&h->dev.st_order, (size_t)h->dev.n_st},  {&h->dev.kg_blk, (size_t)h->dev.n_kg * lcv::kWaves},
+               {&h->dev.kg_cnt, (size_t)h->dev.n_kg},    {&h->dev.kg_off, (size_t)h->dev.n_kg + 1},
+               {&h->dev.kg_ent, nnz_alloc},              {&h->dev.summary, 2}};
+  size_t bytes = 0;
+  for (auto& pt : parts) bytes += (pt.count * sizeof(int32_t) + 255) / 256 * 256;
+  e = hipMalloc(&h->dev.block, bytes);
+  if (e != hipSuccess) {
+    lcv_bsa_layout_destroy(h);
+    return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "hipMalloc of the layout: %s",
+                hipGetErrorString(e));
+  }
+  size_t at = 0;
+  for (auto& pt : parts) {
+    *pt.p = reinterpret_cast<int32_t*>(static_cast<char*>(h->dev.block) + at);
+    at += (pt.count * sizeof(int32_t) + 255) / 256 * 256;
   }
   const lcv::LayoutRule L = make_rule(params);
   e = lcv::launch_layout_build(L, h->dev, stream);
+  int32_t summary[2] = {-1, -1};
+  if (e == hipSuccess) e = hipMemcpyAsync(summary, h->dev.summary, sizeof summary, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  int32_t gpu_nnz = -1;
-  if (e == hipSuccess) e = hipMemcpy(&gpu_nnz, h->dev.row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e != hipSuccess) {
     lcv_bsa_layout_destroy(h);
     return hip_fail(e, "layout build");
   }
-  if (gpu_nnz != info.nnz) {
+  if (summary[0] != info.nnz || summary[1] < 0 || summary[1] > info.nnz) {
     lcv_bsa_layout_destroy(h);
-    return fail(LCV_ERR_HIP, "layout build produced %d entries, expected %lld", gpu_nnz, (long long)info.nnz);
+    return fail(LCV_ERR_HIP, "layout build produced %d entries (expected %lld) and %d key-side entries", summary[0],
+                (long long)info.nnz, summary[1]);
   }
-  // the forward's work order: the workgroup lists by decreasing length in 16 classes of
-  // length (class c holds lengths in [c, c+1) * max / 16), in index order inside a class, so
-  // that neighbouring lists (which share local key blocks) stay together
-  {
-    std::vector<int32_t> cnt(h->dev.n_st), order(h->dev.n_st);
-    e = hipMemcpy(cnt.data(), h->dev.st_cnt, cnt.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
-    int64_t cmax = 1;
-    for (int32_t c : cnt) cmax = c > cmax ? c : cmax;
-    auto cls = [&](int32_t i) { return (int64_t)cnt[i] * 16 / (cmax + 1); };
-    for (int32_t i = 0; i < h->dev.n_st; ++i) order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cls(a) > cls(b); });
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&h->dev.st_order), order.size() * sizeof(int32_t));
-    if (e == hipSuccess)
-      e = hipMemcpy(h->dev.st_order, order.data(), order.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      lcv_bsa_layout_destroy(h);
-      return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "work order of the layout: %s",
-                  hipGetErrorString(e));
-    }
-  }
-  // key-side schedule of the backward
-  const KeyGroups kg = build_key_groups(L);
-  h->dev.n_kg = (int32_t)kg.cnt.size();
-  h->dev.kg_total = (int64_t)kg.ent.size();
-  struct {
-    int32_t** p;
-    const std::vector<int32_t>* v;
-  } kbufs[] = {{&h->dev.kg_blk, &kg.blk}, {&h->dev.kg_cnt, &kg.cnt}, {&h->dev.kg_off, &kg.off},
-               {&h->dev.kg_ent, &kg.ent}};
-  for (auto& b : kbufs) {
-    const size_t bytes = (b.v->empty() ? 1 : b.v->size()) * sizeof(int32_t);
-    e = hipMalloc(reinterpret_cast<void**>(b.p), bytes);
-    if (e == hipSuccess && !b.v->empty())
-      e = hipMemcpy(*b.p, b.v->data(), b.v->size() * sizeof(int32_t), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      lcv_bsa_layout_destroy(h);
-      return fail(e == hipErrorOutOfMemory ? LCV_ERR_OOM : LCV_ERR_HIP, "backward schedule: %s", hipGetErrorString(e));
-    }
-  }
+  h->dev.kg_total = summary[1];
   *out = h;
   return ok();
 }
@@ -503,15 +428,7 @@ lcv_status lcv_bsa_layout_copy_csr(const lcv_bsa_layout* layout, int32_t* row_pt
 
 void lcv_bsa_layout_destroy(lcv_bsa_layout* layout) {
   if (layout == nullptr) return;
-  (void)hipFree(layout->dev.row_ptr);
-  (void)hipFree(layout->dev.col_idx);
-  (void)hipFree(layout->dev.st_cnt);
-  (void)hipFree(layout->dev.st_ent);
-  (void)hipFree(layout->dev.st_order);
-  (void)hipFree(layout->dev.kg_blk);
-  (void)hipFree(layout->dev.kg_cnt);
-  (void)hipFree(layout->dev.kg_off);
-  (void)hipFree(layout->dev.kg_ent);
+  (void)hipFree(layout->dev.block);
   delete layout;
 }
 

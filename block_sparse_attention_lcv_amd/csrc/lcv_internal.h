@@ -127,10 +127,12 @@ struct LayoutDev {
   // of its columns, entry (i << 8) | mask (bit b: query block i attends key block kg_blk[4g+b]).
   int32_t* kg_blk;    // [n_kg * kWaves] key block of each slot, -1 for an empty slot
   int32_t* kg_cnt;    // [n_kg]
-  int32_t* kg_off;    // [n_kg] first entry of each group's list in kg_ent
-  int32_t* kg_ent;    // [kg_total]
+  int32_t* kg_off;    // [n_kg + 1] first entry of each group's list in kg_ent (kg_off[n_kg] = kg_total)
+  int32_t* kg_ent;    // [kg_total] (room for nnz: a group's union is no longer than its columns together)
   int32_t n_kg;
   int64_t kg_total;
+  int32_t* summary;   // [2] written by the build: row_ptr[n] and kg_total, read back once
+  void* block;        // the one device allocation all of the above live in
 };
 
 struct FwdParams {
