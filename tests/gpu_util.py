@@ -100,3 +100,16 @@ def lse_error_budget(q_rot: np.ndarray, k_rot: np.ndarray, mask: np.ndarray, lse
     p_round = var_e * np.sum(p ** 2, axis=1)
     sigma = np.sqrt(q_side + k_side + p_round)
     return worst, sigma
+
+
+def score_rounding_sigma(q: np.ndarray, k: np.ndarray, mask: np.ndarray) -> float:
+    """Standard deviation (natural units, root mean square over the attended pairs) of the
+    score error that the one bf16 rounding of the query operand Q' = bf16(q * log2(e)/8)
+    leaves when q and k are taken as rotated: each product q_c k_c / 8 moves by a
+    round-to-nearest error of relative standard deviation ~0.425 u (u = 2^-8), independently
+    per channel.  q [..., R, 64], k [..., N, 64] with matching leading axes, mask [R, N]."""
+    q2 = np.asarray(q, dtype=np.float64) ** 2
+    k2 = np.asarray(k, dtype=np.float64) ** 2
+    var = (q2 @ np.swapaxes(k2, -1, -2)) / 64.0              # sum_c (q_c k_c / 8)^2
+    m = np.broadcast_to(mask, var.shape)
+    return 0.425 * U_BF16 * float(np.sqrt(np.mean(var[m])))
