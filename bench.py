@@ -36,31 +36,36 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("bsa_fwd_kernel.hip", "attn_tile.h", "lcv_internal.h", "rope_math.h")
+# The kernels whose HBM traffic is taken from counters, with the sources each is built from:
+# a counter summary is valid only for the kernel code it was taken on.
+TRAFFIC_KERNELS = {
+    "bsa_fwd_kernel": ("bsa_fwd_kernel.hip", "attn_tile.h", "lcv_internal.h", "rope_math.h"),
+    "rope3d_kernel": ("rope3d_kernel.hip", "lcv_internal.h", "rope_math.h"),
+    "qk_prologue_kernel": ("qk_prologue_kernel.hip", "lcv_internal.h", "rope_math.h"),
+}
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the attention kernel's sources: a counter summary is valid only for the
-    kernel it was taken on."""
+def kernel_source_hash(kernel: str = "bsa_fwd_kernel") -> str:
+    """sha256 over a kernel's sources."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_attention_lcv_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in TRAFFIC_KERNELS[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def traffic_from_profile(path: str | None):
-    """HBM bytes per launch of the attention kernel from a committed counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration); None when absent or
-    taken on other kernel sources."""
+def traffic_from_profile(path: str | None, kernel: str = "bsa_fwd_kernel"):
+    """HBM bytes per launch of a kernel from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE scaled by the copy-kernel calibration); None when absent or taken on other
+    kernel sources."""
     if not path or not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            data = json.load(f)
-        if data.get("kernel_source_sha256") != kernel_source_hash():
+            data = json.load(f)[kernel]
+        if data.get("kernel_source_sha256") != kernel_source_hash(kernel):
             return None
         return float(data["bytes_per_launch"])
     except Exception:
@@ -83,29 +88,32 @@ def _pmc_rows(directory: str, counter: str):
 
 
 def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str) -> int:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by what the
-    same counters read for a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES)."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, the K RoPE pass and
+    the QK prologue, each scaled by what the same counter reads for a plain copy of COPY_BYTES
+    (read COPY_BYTES, write COPY_BYTES)."""
     result = {}
-    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _pmc_rows(directory, counter)
-        attn = [v for name, v, _ in rows if "bsa_fwd_kernel" in name]
-        # the calibration copies are the largest-grid copy dispatches
-        copy_rows = [(g, v) for name, v, g in rows if "copybuffer" in name.lower() or "copy_kernel" in name.lower()]
-        gmax = max((g for g, _ in copy_rows), default=0)
-        copies = [v for g, v in copy_rows if g == gmax]
-        if not attn or not copies:
-            print(f"no {counter} rows for the attention or copy kernel in {directory}", file=sys.stderr)
-            return 1
-        copy_kib = float(np.median(copies))
-        scale = COPY_BYTES / (copy_kib * 1024.0)
-        result[counter] = {"attn_kib_per_launch": float(np.median(attn)), "copy_kib": copy_kib,
-                           "scale_bytes_per_kib": scale * 1024.0, "launches": len(attn)}
-    fetch = result["FETCH_SIZE"]["attn_kib_per_launch"] * result["FETCH_SIZE"]["scale_bytes_per_kib"]
-    write = result["WRITE_SIZE"]["attn_kib_per_launch"] * result["WRITE_SIZE"]["scale_bytes_per_kib"]
-    result["bytes_per_launch"] = fetch + write
-    result["kernel_source_sha256"] = kernel_source_hash()
-    result["fetch_bytes"] = fetch
-    result["write_bytes"] = write
+    for kernel in TRAFFIC_KERNELS:
+        entry = {}
+        for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            rows = _pmc_rows(directory, counter)
+            vals = [v for name, v, _ in rows if kernel in name]
+            # the calibration copies are the largest-grid copy dispatches
+            copy_rows = [(g, v) for name, v, g in rows
+                         if "copybuffer" in name.lower() or "copy_kernel" in name.lower()]
+            gmax = max((g for g, _ in copy_rows), default=0)
+            copies = [v for g, v in copy_rows if g == gmax]
+            if not vals or not copies:
+                print(f"no {counter} rows for {kernel} or the copy kernel in {directory}", file=sys.stderr)
+                return 1
+            copy_kib = float(np.median(copies))
+            scale = COPY_BYTES / (copy_kib * 1024.0)
+            entry[counter] = {"kib_per_launch": float(np.median(vals)), "copy_kib": copy_kib,
+                              "scale_bytes_per_kib": scale * 1024.0, "launches": len(vals)}
+        fetch = entry["FETCH_SIZE"]["kib_per_launch"] * entry["FETCH_SIZE"]["scale_bytes_per_kib"]
+        write = entry["WRITE_SIZE"]["kib_per_launch"] * entry["WRITE_SIZE"]["scale_bytes_per_kib"]
+        entry.update({"bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+                      "kernel_source_sha256": kernel_source_hash(kernel)})
+        result[kernel] = entry
     with open(out_path, "w") as f:
         json.dump(result, f, indent=1)
     print(json.dumps(result))
@@ -212,7 +220,7 @@ def timed_launches(torch, stream, launch, count: int) -> float:
     return a.elapsed_time(b) / count
 
 
-def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
+def measure_prologue(bsa, torch, q, k, w, steps: int, stream, traffic_json: str | None = None) -> dict:
     """The QK prologue (RMSNorm of each head's channels + 3D-RoPE) on this workload's Q and
     K, timed apart from the attention step: HBM-bound, algorithmic bytes = bf16 read + write
     of every element (4 B per element per launch)."""
@@ -230,6 +238,7 @@ def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
     ms = timed_launches(torch, stream, both, steps) / 2
     nbytes = 4.0 * q.numel()
     gbps = nbytes / (ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(traffic_json, "qk_prologue_kernel") if traffic_json else None
     # a plain device copy of the same tensor: the HBM rate a read + write stream reaches here
     for _ in range(3):
         qn.copy_(q)
@@ -240,7 +249,7 @@ def measure_prologue(bsa, torch, q, k, w, steps: int, stream) -> dict:
     return {"bound": "hbm", "kernel": "qk_prologue_kernel", "avg_launch_ms": round(ms, 4),
             "bytes_per_launch": nbytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBS, 4), "launches": 2 * steps,
-            "copy_reference_gbs": round(copy_gbps, 1),
+            "copy_reference_gbs": round(copy_gbps, 1), "traffic": traffic,
             "what": "RMSNorm over each head's 64 channels with a 64-value gain, then 3D-RoPE, on Q and on K"}
 
 
@@ -423,7 +432,7 @@ def main() -> int:
     ap.add_argument("--no-merge", action="store_true",
                     help="skip the separate measurement of the merge of partial attention results")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "bsa_fwd_t2v720_traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "t2v720_traffic.json"))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -556,6 +565,31 @@ def main() -> int:
 
     default_config = (args.workload == "t2v720" and not args.cached and not args.shard_of
                       and args.rope_mode == "k-pass" and args.local is None and args.stride is None)
+    # the side passes as HBM-bound passes: the K RoPE pass (bf16 read + write of every
+    # element of K, timed by the step's events) and the layout build (its outputs: the CSR,
+    # the workgroup lists, the work order and the backward's key-side schedule, all written
+    # once; timed on the host around a warm build: allocation, 9 kernels and one read-back)
+    rope_pass = None
+    if args.rope_mode == "k-pass":
+        rope_avg = float(np.mean(rope_ms))
+        rope_bytes = 4.0 * k.numel()
+        rope_gbs = rope_bytes / (rope_avg * 1e-3) / 1e9
+        rope_pass = {"bound": "hbm", "kernel": "rope3d_kernel", "avg_launch_ms": round(rope_avg, 4),
+                     "bytes_per_launch": rope_bytes, "achieved": round(rope_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(rope_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(args.traffic_json, "rope3d_kernel") if default_config else None,
+                     "what": "3D-RoPE of K (bf16 in, fp32 math, bf16 out) into a second buffer, every step"}
+    n_st = -(-info["n_blocks"] // 4)
+    # row_ptr, col_idx, the workgroup lists and counts, the work order, and the key groups'
+    # blocks, counts and offsets (their column lists, at most nnz entries, are not counted)
+    layout_bytes = 4.0 * ((info["n_blocks"] + 1) + 2 * info["nnz"] + 2 * n_st + 6 * n_st + 1)
+    layout_gbs = layout_bytes / (layout_ms * 1e-3) / 1e9
+    layout_build = {"bound": "launch", "ms": round(layout_ms, 4), "bytes": layout_bytes,
+                    "achieved": round(layout_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(layout_gbs / HBM_PEAK_GBS, 6),
+                    "what": "warm lcv_bsa_build_layout on the host clock: one allocation, 9 kernels (row counts, "
+                            "scans, CSR fill, workgroup list unions, work order, key-group unions) and one "
+                            "read-back; bytes = every array written once except the key groups' column lists"}
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -599,12 +633,15 @@ def main() -> int:
             "avg_launch_ms": round(avg_launch_ms, 4),
         },
         "rope_pass_ms": round(float(np.mean(rope_ms)), 4) if args.rope_mode == "k-pass" else None,
+        "rope_pass": rope_pass,
+        "layout_build": layout_build,
     }
     # the other kernels are measured on the full call's tensors
     q = q_full
     extras = not args.cached and not args.shard_of
     if not args.no_prologue and extras:
-        result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream)
+        result["qk_prologue"] = measure_prologue(bsa, torch, q, k, w, args.steps, stream,
+                                                 args.traffic_json if default_config else None)
     if not args.no_backward and extras:
         result["backward"] = measure_backward(bsa, torch, q, k, v, layout, w, flops, args.steps, stream)
         if not args.no_prologue:

@@ -36,6 +36,15 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
 }
 
+// Raw buffer resource (no stride, 32-bit data format) over `bytes` bytes from the byte address
+// `base`, both wave-uniform: buffer loads at offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(uint64_t base, int bytes) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  bytes = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
+}
+
 // 8 bf16 channels -> bf16(value * log2(e)/8), each product in fp32 and rounded to nearest
 // even: the forward's query operand, and the backward's (from the same bits, the same
 // bits out).

@@ -116,23 +116,30 @@ __device__ __forceinline__ bf16x8 tr_read(const unsigned char* tile, const TrOff
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Asynchronous copy of rows 64*blk .. 64*blk+63 (clamped to the sequence) of a [N, 64] bf16
-// slice into an LDS tile: wavefront w moves rows 8w .. 8w+7, lane l row 8w + l/8, landing at
-// physical chunk l%8, which holds logical chunk (l%8) ^ swz(row) of the swizzle.
+// Asynchronous copy of rows 64*blk .. 64*blk+63 of a [N, 64] bf16 slice into an LDS tile by a
+// buffer load straight into LDS: wavefront w moves rows 8w .. 8w+7, lane l row 8w + l/8,
+// landing at physical chunk l%8, which holds logical chunk (l%8) ^ swz(row) of the swizzle.
+// The block's first row is the base of a buffer resource (scalar arithmetic) whose size ends at
+// row N, so rows past the sequence read zeros (their scores are masked, their probabilities and
+// dS are zero); the lane's offset inside the block does not depend on the block.
 __device__ __forceinline__ void copy_tile(const uint16_t* slice, int32_t N, int blk, unsigned char* dst, int wave,
                                           int lane) {
   const int row = 8 * wave + (lane >> 3);
-  int t = 64 * blk + row;
-  t = t < N ? t : N - 1;
   const int gch = (lane & 7) ^ swz(row);
-  __builtin_amdgcn_global_load_lds(slice + (int64_t)t * 64 + 8 * gch, (lds_void*)(dst + 1024 * wave), 16, 0, 0);
+  int rows = N - 64 * blk;
+  rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc((uint64_t)(uintptr_t)slice + (uint64_t)blk * kTileBytes, rows * 128);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * wave), 16, (uint32_t)(row * 128 + 16 * gch), 0,
+                                           0, 0);
 }
 
-// Asynchronous copy of 64 fp32 row values (clamped) into LDS (one wavefront).
+// Asynchronous copy of the 64 fp32 row values of block blk into LDS (one wavefront), zeros past
+// row N.
 __device__ __forceinline__ void copy_rows_f32(const float* slice, int32_t N, int blk, float* dst, int lane) {
-  int t = 64 * blk + lane;
-  t = t < N ? t : N - 1;
-  __builtin_amdgcn_global_load_lds(slice + t, (lds_void*)dst, 4, 0, 0);
+  int rows = N - 64 * blk;
+  rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc((uint64_t)(uintptr_t)(slice + (int64_t)64 * blk), rows * 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(4 * lane), 0, 0, 0);
 }
 
 // D = rowsum(dO * O), lse * log2(e) and Q' = bf16(Q * log2(e)/8) per row; one thread per

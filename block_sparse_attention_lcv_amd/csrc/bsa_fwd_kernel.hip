@@ -99,13 +99,9 @@ static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;   // scalar loads of the lists
 
-// Raw buffer resource (no stride, 32-bit data format) over `rows` key rows of 128 bytes from
-// the byte address `base`; both wave-uniform.
+// Buffer resource over `rows` key rows of 128 bytes from the byte address `base`.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(uint64_t base, int rows) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  const int bytes = __builtin_amdgcn_readfirstlane(rows * 128);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
+  return uniform_rsrc(base, rows * 128);
 }
 
 // Lane offset (bytes) of load c inside a K or V block: row 8u + l/8, physical chunk l%8
