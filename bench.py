@@ -83,7 +83,9 @@ def _pmc_rows(directory: str, counter: str):
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r.get("Counter_Name") == counter:
-                    rows.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"]),
+                                 int(r.get("Dispatch_Id") or 0)))
+    rows.sort(key=lambda r: r[2])
     return rows
 
 
@@ -97,13 +99,16 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str) -> int:
         for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             rows = _pmc_rows(directory, counter)
             vals = [v for name, v, _ in rows if kernel in name]
-            # the calibration copies are the largest-grid copy dispatches
-            copy_rows = [(g, v) for name, v, g in rows
-                         if "copybuffer" in name.lower() or "copy_kernel" in name.lower()]
-            gmax = max((g for g, _ in copy_rows), default=0)
-            copies = [v for g, v in copy_rows if g == gmax]
-            if not vals or not copies:
+            # the calibration copies are the last three copy dispatches of the run (bench.py
+            # --copy-calibration issues them after everything else); other copies (the plain
+            # copy of Q beside the RoPE pass) have other sizes
+            copies = [v for name, v, _ in rows
+                      if "copybuffer" in name.lower() or "copy_kernel" in name.lower()][-3:]
+            if not vals or len(copies) < 3:
                 print(f"no {counter} rows for {kernel} or the copy kernel in {directory}", file=sys.stderr)
+                return 1
+            if max(copies) > 1.01 * min(copies):
+                print(f"{counter}: the last three copies disagree ({copies})", file=sys.stderr)
                 return 1
             copy_kib = float(np.median(copies))
             scale = COPY_BYTES / (copy_kib * 1024.0)

@@ -40,3 +40,46 @@ def test_bench_refuses_several_gpus():
                          timeout=120, cwd=root)
     assert res.returncode == 2
     assert "one GPU" in res.stderr + res.stdout
+
+
+def _write_pmc(directory, counter, rows):
+    import csv
+    import os
+    os.makedirs(directory, exist_ok=True)
+    with open(os.path.join(directory, "x_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+def test_traffic_calibration_uses_the_last_three_copies(tmp_path):
+    """The HBM byte counts scale each counter by the 1 GiB calibration copies that end the
+    run; a copy of another size earlier in the run (the plain copy of Q) must not enter it."""
+    import json
+    kib = bench.COPY_BYTES // 1024
+    copy = "__amd_rocclr_copyBuffer"
+    fetch = [(copy, 1.5), ("void lcv::bsa_fwd_kernel<true>", 1000.0), ("lcv::rope3d_kernel", 300.0),
+             ("void lcv::qk_prologue_kernel<true>", 310.0)] + [(copy, 100.0)] * 5 + [(copy, kib / 2)] * 3
+    write = [(copy, 0.03), ("void lcv::bsa_fwd_kernel<true>", 400.0), ("lcv::rope3d_kernel", 600.0),
+             ("void lcv::qk_prologue_kernel<true>", 600.0)] + [(copy, 200.0)] * 5 + [(copy, kib)] * 3
+    _write_pmc(tmp_path / "f", "FETCH_SIZE", fetch)
+    _write_pmc(tmp_path / "w", "WRITE_SIZE", write)
+    out = tmp_path / "t.json"
+    assert bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(out)) == 0
+    d = json.loads(out.read_text())
+    assert d["bsa_fwd_kernel"]["fetch_bytes"] == 1000.0 * 2048
+    assert d["bsa_fwd_kernel"]["write_bytes"] == 400.0 * 1024
+    assert d["rope3d_kernel"]["bytes_per_launch"] == 300.0 * 2048 + 600.0 * 1024
+    assert d["qk_prologue_kernel"]["FETCH_SIZE"]["copy_kib"] == kib / 2
+    assert bench.traffic_from_profile(str(out), "rope3d_kernel") == 300.0 * 2048 + 600.0 * 1024
+
+
+def test_traffic_calibration_refuses_disagreeing_copies(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    rows = [("void lcv::bsa_fwd_kernel<true>", 1.0), ("lcv::rope3d_kernel", 1.0),
+            ("void lcv::qk_prologue_kernel<true>", 1.0), (copy, 100.0), (copy, 500.0), (copy, 500.0)]
+    _write_pmc(tmp_path / "f", "FETCH_SIZE", rows)
+    _write_pmc(tmp_path / "w", "WRITE_SIZE", rows)
+    assert bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t.json")) == 1
