@@ -97,7 +97,11 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 raw, int c, const Coords& xyz,
 constexpr int kLoadsPerWave = 8 / kWaves;
 static_assert(8 % kWaves == 0, "a tile is 8 wave-loads");
 
-typedef __attribute__((address_space(4))) const int32_t const_i32;   // scalar loads of the lists
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// s_waitcnt immediate that waits for every LDS operation only (vmcnt 63 in bits 3:0 and
+// 15:14, expcnt 7 in bits 6:4, lgkmcnt 0 in bits 11:8)
+constexpr int kWaitLdsOnly = 0xC07F;   // scalar loads of the lists
 
 // Buffer resource over `rows` key rows of 128 bytes from the byte address `base`.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(uint64_t base, int rows) {
@@ -260,37 +264,19 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   static_assert(!CROSS || (!ROPE_Q && !ROPE_K && !CACHED), "cross-attention has no RoPE and no cache");
   // LDS: the K and V tiles of stages 0 and 1 are four separate variables, so the compiler
   // can tell that reads of one stage do not depend on the global -> LDS copies into the
-  // other (with one shared array it makes those reads wait for every copy in flight); the
-  // dynamic part holds the cos/sin table.
+  // other (with one shared array it makes those reads wait for every copy in flight).
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // cos/sin table of the fused RoPE (its own variable, so that the compiler can tell its
+  // writes apart from the copies into the stages)
+  __shared__ __attribute__((aligned(16))) float2 lds_tab[(ROPE_Q || ROPE_K) ? kMaxRopeEntries : 1];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 5;
   const int l32 = lane & 31;
-
-  // ---- cos/sin table of every (axis, position, pair) of the grid
-  float2* tab = reinterpret_cast<float2*>(smem);
-  if constexpr (ROPE_Q || ROPE_K) {
-    for (int e = tid; e < P.rope_entries; e += kThreads) {
-      int pos, p, width;
-      if (e < 8 * P.T) {
-        pos = e >> 3; p = e & 7; width = 16;
-      } else if (e < 8 * P.T + 12 * P.H) {
-        const int r = e - 8 * P.T;
-        pos = r / 12; p = r - 12 * pos; width = 24;
-      } else {
-        const int r = e - 8 * P.T - 12 * P.H;
-        pos = r / 12; p = r - 12 * pos; width = 24;
-      }
-      tab[e] = rope_cos_sin(pos, p, width, P.log2_theta);
-    }
-    __syncthreads();
-  }
 
   // ---- work item (a (batch, head) and a workgroup list of 4 query blocks): XCD x (=
   // blockIdx % 8) runs the x-th contiguous eighth of the items, head after head, so that the
@@ -316,6 +302,33 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   }
   const KvSrc kvs = kv_src<CACHED, CROSS>(P, bh, key_end);
 
+  // the workgroup's list: layout-built (self-attention), or every text block for all four
+  // wavefronts (cross-attention)
+  const const_i32* ents = CROSS ? nullptr : (const const_i32*)P.st_ent + P.row_ptr[st * kWaves];
+  const int cnt = CROSS ? (key_end + 63) >> 6 : P.st_cnt[st];
+  auto entry = [&](int e) __attribute__((always_inline)) {
+    if constexpr (CROSS)
+      return (e << 8) | ((1 << kWaves) - 1);
+    else
+      return (int)ents[e];
+  };
+
+  // List entries are wave-uniform (SGPRs, scalar loads): entry e+1 is known when step e
+  // starts (its block is copied during step e) and entry e+2 is loaded during step e.  The
+  // copies of the first block go out before the cos/sin table and the query block are
+  // prepared, so that the list lookups and the copies overlap that work.
+  u32x4 kreg[kLoadsPerWave];
+  uint32_t voff[kLoadsPerWave];
+#pragma unroll
+  for (int c = 0; c < kLoadsPerWave; ++c) voff[c] = stage_lane_offset(wave, lane, c);
+  int ent_cur = 0, ent_next = 0;
+  if (cnt > 0) {
+    ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
+    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
+    const int j0 = ent_cur >> 8;
+    stage_issue<ROPE_K, CACHED>(kvs, lds_k0, lds_v0, j0, wave, lane, voff, kreg);
+  }
+
   // ---- this wavefront's query block as MFMA B operands: qf[qt][ks] holds rows
   // 32*qt + (lane & 31), channels 16*ks + 8*(lane >> 5) .. +7, scaled by log2(e)/8
   const int qblk = st * kWaves + wave;
@@ -323,22 +336,55 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   bf16x8 qf[2][4];
   int qtok[2];
   bool qok[2];
+  // all eight 16-byte loads go out before any is used (rows outside the call's range read a
+  // valid row of the tensor and are zeroed afterwards), so the block costs one memory latency
+  u32x4 qraw[2][4];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     qtok[qt] = 64 * qblk + 32 * qt + l32;
     qok[qt] = wave_on && qtok[qt] >= P.q_row0 && qtok[qt] < P.q_end;
-    const uint16_t* qrow = P.q + ((int64_t)bh * P.q_rows + (qtok[qt] - P.q_row0)) * 64;
+    int qr = qtok[qt] - P.q_row0;
+    qr = qr < 0 ? 0 : (qr < P.q_rows ? qr : P.q_rows - 1);
+    const uint16_t* qrow = P.q + ((int64_t)bh * P.q_rows + qr) * 64;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qraw[qt][ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * ks + g));
+  }
+  // ---- cos/sin table of every (axis, position, pair) of the grid
+  float2* tab = lds_tab;
+  if constexpr (ROPE_Q || ROPE_K) {
+    for (int e = tid; e < P.rope_entries; e += kThreads) {
+      int pos, p, width;
+      if (e < 8 * P.T) {
+        pos = e >> 3; p = e & 7; width = 16;
+      } else if (e < 8 * P.T + 12 * P.H) {
+        const int r = e - 8 * P.T;
+        pos = r / 12; p = r - 12 * pos; width = 24;
+      } else {
+        const int r = e - 8 * P.T - 12 * P.H;
+        pos = r / 12; p = r - 12 * pos; width = 24;
+      }
+      tab[e] = rope_cos_sin(pos, p, width, P.log2_theta);
+    }
+    // the table's LDS writes are visible to the workgroup; the first block's copies stay in
+    // flight (a fenced barrier would wait for them here)
+    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  }
+
+  // rotation (fused Q RoPE) and scaling of the loaded query block
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
     Coords xyz{0u, 0u, 0u};
     if (ROPE_Q && qok[qt]) xyz = token_coords((uint32_t)qtok[qt], P);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + g;
-      u32x4 raw{0u, 0u, 0u, 0u};
-      if (qok[qt]) {
-        raw = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
-        if constexpr (ROPE_Q) raw = rope_chunk(raw, c, xyz, tab, P);
-        raw = scale_chunk_log2(raw);
-      }
+      u32x4 raw = qraw[qt][ks];
+      if constexpr (ROPE_Q) raw = rope_chunk(raw, c, xyz, tab, P);
+      raw = scale_chunk_log2(raw);
+      if (!qok[qt]) raw = u32x4{0u, 0u, 0u, 0u};
       qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -369,30 +415,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   float lsum[2] = {0.f, 0.f};
   bool ref_nonzero = false;                 // some row of the wavefront has a reference other than 0
 
-  // the workgroup's list: layout-built (self-attention), or every text block for all four
-  // wavefronts (cross-attention)
-  const const_i32* ents = CROSS ? nullptr : (const const_i32*)P.st_ent + P.row_ptr[st * kWaves];
-  const int cnt = CROSS ? (key_end + 63) >> 6 : P.st_cnt[st];
-  auto entry = [&](int e) __attribute__((always_inline)) {
-    if constexpr (CROSS)
-      return (e << 8) | ((1 << kWaves) - 1);
-    else
-      return (int)ents[e];
-  };
-
-  // List entries are wave-uniform (SGPRs, scalar loads): entry e+1 is known when step e
-  // starts (its block is copied during step e) and entry e+2 is loaded during step e.
-  u32x4 kreg[kLoadsPerWave];
-  uint32_t voff[kLoadsPerWave];
-#pragma unroll
-  for (int c = 0; c < kLoadsPerWave; ++c) voff[c] = stage_lane_offset(wave, lane, c);
-  int ent_cur = 0, ent_next = 0;
-  if (cnt > 0) {
-    ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
-    if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
-    const int j0 = ent_cur >> 8;
-    stage_issue<ROPE_K, CACHED>(kvs, lds_k0, lds_v0, j0, wave, lane, voff, kreg);
-    if constexpr (ROPE_K) stage_store_k(P, lds_k0, j0, wave, lane, tab, kreg);
+  // the first block's K rotated into its stage (fused K RoPE), then every copy of it landed
+  if constexpr (ROPE_K) {
+    if (cnt > 0) stage_store_k(P, lds_k0, ent_cur >> 8, wave, lane, tab, kreg);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -634,7 +659,7 @@ hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.n_items == 0) return hipSuccess;
   const unsigned groups = item_groups(p.n_items);
   const bool rq = (p.flags & LCV_ROPE_Q) != 0, rk = (p.flags & LCV_ROPE_K) != 0, cached = p.kv_split > 0;
-  const size_t lds = (rq || rk) ? (size_t)p.rope_entries * sizeof(float2) : 0;
+  const size_t lds = 0;   // all LDS is static
   const int v = (rq ? 4 : 0) | (rk ? 2 : 0) | (cached ? 1 : 0);
   switch (v) {
     case 0: return launch_variant<false, false, false>(p, groups, lds, stream);
