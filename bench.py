@@ -99,6 +99,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str) -> int:
         for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             rows = _pmc_rows(directory, counter)
             vals = [v for name, v, _ in rows if kernel in name]
+            if not vals and kernel != "bsa_fwd_kernel":
+                break   # a side pass this run did not launch
             # the calibration copies are the last three copy dispatches of the run (bench.py
             # --copy-calibration issues them after everything else); other copies (the plain
             # copy of Q beside the RoPE pass) have other sizes
@@ -114,6 +116,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str) -> int:
             scale = COPY_BYTES / (copy_kib * 1024.0)
             entry[counter] = {"kib_per_launch": float(np.median(vals)), "copy_kib": copy_kib,
                               "scale_bytes_per_kib": scale * 1024.0, "launches": len(vals)}
+        if len(entry) < 2:
+            continue
         fetch = entry["FETCH_SIZE"]["kib_per_launch"] * entry["FETCH_SIZE"]["scale_bytes_per_kib"]
         write = entry["WRITE_SIZE"]["kib_per_launch"] * entry["WRITE_SIZE"]["scale_bytes_per_kib"]
         entry.update({"bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
@@ -123,6 +127,35 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str) -> int:
         json.dump(result, f, indent=1)
     print(json.dumps(result))
     return 0
+
+
+def summarize_counters(directory: str) -> int:
+    """Per-kernel averages over the dispatches of every counter in a rocprofv3 --pmc run
+    (one JSON object per kernel name), with the matrix-core utilisation where the run has
+    the counters for it: SQ_VALU_MFMA_BUSY_CYCLES / (128 * GRBM_GUI_ACTIVE), the busy count
+    being summed over the 1,024 SIMDs and GRBM_GUI_ACTIVE over the 8 XCDs."""
+    import csv
+    import glob
+    import re
+    acc: dict = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                m = re.search(r"::(\w+_kernel(<[^>]*>)?)", r["Kernel_Name"])
+                name = m.group(1) if m else r["Kernel_Name"][:60]
+                acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for name, counters in acc.items():
+        out = {"kernel": name, "dispatches": max(len(v) for v in counters.values())}
+        avg = {c: float(np.mean(v)) for c, v in counters.items()}
+        out.update({c: round(v, 1) for c, v in avg.items()})
+        if avg.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            out["mfma_busy"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (128 * avg["GRBM_GUI_ACTIVE"]), 4)
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            out["coexec_of_mfma_busy"] = round(avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+        if avg.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in avg:
+            out["valu_per_mfma"] = round(avg["SQ_INSTS_VALU"] / avg["SQ_INSTS_MFMA"], 3)
+        print(json.dumps(out))
+    return 0 if acc else 1
 
 
 def cpu_baseline(w, seconds: float = 12.0) -> dict:
@@ -443,7 +476,11 @@ def main() -> int:
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --copy-calibration into "
                          "HBM bytes per attention launch; writes --traffic-json and exits")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="print per-kernel averages of every counter of one rocprofv3 --pmc run and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.traffic_json)
 
