@@ -83,3 +83,26 @@ def test_traffic_calibration_refuses_disagreeing_copies(tmp_path):
     _write_pmc(tmp_path / "f", "FETCH_SIZE", rows)
     _write_pmc(tmp_path / "w", "WRITE_SIZE", rows)
     assert bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t.json")) == 1
+
+
+def test_counter_summary_per_kernel(tmp_path, capsys):
+    """--summarize-counters: per-kernel means over the dispatches and the matrix-core share
+    SQ_VALU_MFMA_BUSY_CYCLES / (128 * GRBM_GUI_ACTIVE)."""
+    import csv
+    import json
+    d = tmp_path / "pmc"
+    d.mkdir()
+    with open(d / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        name = "void lcv::(anonymous namespace)::bsa_fwd_kernel<true, false, false, false>(lcv::FwdParams)"
+        for i, (busy, gui, mfma, valu) in enumerate(((1280.0, 20.0, 40.0, 250.0), (1920.0, 30.0, 60.0, 390.0))):
+            for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", gui), ("SQ_INSTS_MFMA", mfma),
+                         ("SQ_INSTS_VALU", valu)):
+                w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+    assert bench.summarize_counters(str(d)) == 0
+    out = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
+    assert len(out) == 1 and out[0]["kernel"] == "bsa_fwd_kernel<true, false, false, false>"
+    assert out[0]["dispatches"] == 2
+    assert out[0]["mfma_busy"] == round(1600.0 / (128 * 25.0), 4)
+    assert out[0]["valu_per_mfma"] == round(320.0 / 50.0, 3)
