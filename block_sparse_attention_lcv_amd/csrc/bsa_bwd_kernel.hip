@@ -66,6 +66,18 @@ __device__ __forceinline__ bf16x8 fold_neg(float m, int g) {
   return g == 0 ? v : zero;
 }
 
+// The three parts of fold_neg(m) packed in 8 bytes (hi | mid << 16, lo), as the backward's
+// prep pass stores them per row, and the operand rebuilt from them (bitwise fold_neg(m, g)).
+__device__ __forceinline__ uint2 fold_parts(float m) {
+  const bf16x8 v = fold_neg(m, 0);
+  const u32x4 w = __builtin_bit_cast(u32x4, v);
+  return uint2{w[0], w[1]};
+}
+__device__ __forceinline__ bf16x8 fold_operand(uint2 parts, int g) {
+  const u32x4 w = {g == 0 ? parts.x : 0u, g == 0 ? parts.y : 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 __device__ __forceinline__ bf16x8 ones_slots(int g) {
   const __bf16 one = (__bf16)1.0f, z = (__bf16)0.0f;
   return g == 0 ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
@@ -142,11 +154,23 @@ __device__ __forceinline__ void copy_rows_f32(const float* slice, int32_t N, int
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(4 * lane), 0, 0, 0);
 }
 
-// D = rowsum(dO * O), lse * log2(e) and Q' = bf16(Q * log2(e)/8) per row; one thread per
-// 8-channel chunk of a row.
+// Asynchronous copy of the 64 eight-byte row values of block blk into LDS (one wavefront, two
+// 4-byte loads per lane), zeros past row N.
+__device__ __forceinline__ void copy_rows_u64(const uint2* slice, int32_t N, int blk, uint2* dst, int lane) {
+  int rows = N - 64 * blk;
+  rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc((uint64_t)(uintptr_t)(slice + (int64_t)64 * blk), rows * 8);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(4 * lane), 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(reinterpret_cast<unsigned char*>(dst) + 256), 4,
+                                           (uint32_t)(256 + 4 * lane), 0, 0, 0);
+}
+
+// D = rowsum(dO * O), lse * log2(e) and Q' = bf16(Q * log2(e)/8) per row, and the key walk's
+// fold operands of -lse * log2(e) and -D (their three bf16 parts); one thread per 8-channel
+// chunk of a row.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* q, const uint16_t* out, const uint16_t* dout,
                                                        const float* lse, uint16_t* qs, float* lse2, float* delta,
-                                                       int64_t rows) {
+                                                       uint2* fold_l, uint2* fold_d, int64_t rows) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid >> 3;
   const int c = (int)(gid & 7);
@@ -167,7 +191,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* q, const 
   if (c == 0) {
     delta[row] = s;
     const float l = lse[row];
-    lse2[row] = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
+    const float l2 = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
+    lse2[row] = l2;
+    fold_l[row] = fold_parts(l2);
+    fold_d[row] = fold_parts(s);
   }
 }
 
@@ -601,10 +628,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   __shared__ __attribute__((aligned(1024))) unsigned char lds_q1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_o0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_o1[kTileBytes];
-  __shared__ __attribute__((aligned(256))) float lds_l0[64];
-  __shared__ __attribute__((aligned(256))) float lds_l1[64];
-  __shared__ __attribute__((aligned(256))) float lds_d0[64];
-  __shared__ __attribute__((aligned(256))) float lds_d1[64];
+  __shared__ __attribute__((aligned(512))) uint2 lds_l0[64];   // fold parts of -lse * log2(e) per query row
+  __shared__ __attribute__((aligned(512))) uint2 lds_l1[64];
+  __shared__ __attribute__((aligned(512))) uint2 lds_d0[64];   // and of -D
+  __shared__ __attribute__((aligned(512))) uint2 lds_d1[64];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -672,13 +699,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   };
   const uint16_t* qslice = P.qs + base * 64;
   const uint16_t* oslice = P.dout + base * 64;
-  const float* lslice = P.lse2 + base;
-  const float* dslice = P.delta + base;
-  auto copies = [&](int blk, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
+  const uint2* lslice = P.fold_l + base;
+  const uint2* dslice = P.fold_d + base;
+  auto copies = [&](int blk, unsigned char* qd, unsigned char* od, uint2* ld, uint2* dd) __attribute__((always_inline)) {
     copy_tile(qslice, P.N, blk, qd, wave, lane);
     copy_tile(oslice, P.N, blk, od, wave, lane);
-    if (wave == 0) copy_rows_f32(lslice, P.N, blk, ld, lane);
-    if (wave == 1) copy_rows_f32(dslice, P.N, blk, dd, lane);
+    if (wave == 0) copy_rows_u64(lslice, P.N, blk, ld, lane);
+    if (wave == 1) copy_rows_u64(dslice, P.N, blk, dd, lane);
   };
   int ent_cur = 0, ent_next = 0;
   if (cnt > 0) {
@@ -691,7 +718,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
 
   // S' - lse * log2(e) (S' = Q' K^T, log2 units) and dP - D for queries 32qt .. 32qt+31 (registers) and the wavefront's keys
   // (lanes); the per-query lse and D enter through one folded MFMA step each
-  auto sdp_half = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int qt,
+  auto sdp_half = [&](const unsigned char* qb, const unsigned char* ob, const uint2* lb, const uint2* db, int qt,
                       f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     bf16x8 qa[4], oa[4];
 #pragma unroll
@@ -699,8 +726,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       qa[ks] = *reinterpret_cast<const bf16x8*>(qb + qa_off[ks] + 4096u * qt);
       oa[ks] = *reinterpret_cast<const bf16x8*>(ob + qa_off[ks] + 4096u * qt);
     }
-    const bf16x8 fold_l = fold_neg(lb[32 * qt + l32], g);
-    const bf16x8 fold_d = fold_neg(db[32 * qt + l32], g);
+    const bf16x8 fold_l = fold_operand(lb[32 * qt + l32], g);
+    const bf16x8 fold_d = fold_operand(db[32 * qt + l32], g);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_l, ones, f32x16{}, 0, 0, 0);
     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_d, ones, f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -745,7 +772,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   // One query block, its halves software-pipelined: the second half's S and dP go to the
   // matrix cores while the vector ALU forms the first half's P and dS, and the first half's
   // dV^T, dK^T updates run with the second half's P and dS.
-  auto block = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db, int i,
+  auto block = [&](const unsigned char* qb, const unsigned char* ob, const uint2* lb, const uint2* db, int i,
                    auto mask_tag, auto&& copies) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s0, dp0, s1, dp1;
@@ -777,8 +804,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     constexpr int STAGE = decltype(stage_tag)::value;
     const unsigned char* const qc = STAGE ? lds_q1 : lds_q0;
     const unsigned char* const oc = STAGE ? lds_o1 : lds_o0;
-    const float* const lc = STAGE ? lds_l1 : lds_l0;
-    const float* const dc = STAGE ? lds_d1 : lds_d0;
+    const uint2* const lc = STAGE ? lds_l1 : lds_l0;
+    const uint2* const dc = STAGE ? lds_d1 : lds_d0;
     const int ent = ent_cur;
     const int in = ent_next >> 8;
     auto next_copies = [&]() __attribute__((always_inline)) {
@@ -900,7 +927,7 @@ hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.bh_rows > 0) {
     const int64_t threads = p.bh_rows * 8;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.q, p.out,
-                       p.dout, p.lse, p.qs, p.lse2, p.delta, p.bh_rows);
+                       p.dout, p.lse, p.qs, p.lse2, p.delta, p.fold_l, p.fold_d, p.bh_rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (!cross) {

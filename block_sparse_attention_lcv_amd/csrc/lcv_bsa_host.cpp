@@ -224,8 +224,9 @@ lcv_status forward_common(const FwdArgs& a, int32_t batch, int32_t heads, const 
 }
 
 // Workspace of the attention backward, per query row: Q' = bf16(q * log2(e)/8) (64 bf16 = 32
-// fp32 slots), then lse * log2(e) and D = rowsum(dO * O) of every row.
-constexpr int64_t kBwdRowFloats = 34;
+// fp32 slots), then lse * log2(e) and D = rowsum(dO * O) of every row, then the three bf16
+// parts of -lse * log2(e) and of -D (8 bytes each) of every row.
+constexpr int64_t kBwdRowFloats = 38;
 
 // Work split of the cross-attention backward: the query walk takes four query blocks per
 // workgroup; the key walk takes four text blocks and one chunk of the query blocks, with
@@ -619,6 +620,8 @@ lcv_status lcv_cross_attention_backward(const void* q, const void* k, const void
   p.qs = reinterpret_cast<uint16_t*>(workspace);
   p.lse2 = workspace + 32 * bh * n_q;
   p.delta = p.lse2 + bh * n_q;
+  p.fold_l = reinterpret_cast<uint2*>(p.delta + bh * n_q);
+  p.fold_d = p.fold_l + bh * n_q;
   p.cross = true;
   p.part_dk = workspace + pl.part_offset;
   p.part_dv = p.part_dk + pl.part_floats;
@@ -690,6 +693,8 @@ lcv_status lcv_bsa_backward(const void* q, const void* k, const void* v, const v
   p.qs = reinterpret_cast<uint16_t*>(workspace);
   p.lse2 = workspace + 32 * bh * N;
   p.delta = p.lse2 + bh * N;
+  p.fold_l = reinterpret_cast<uint2*>(p.delta + bh * N);
+  p.fold_d = p.fold_l + bh * N;
   p.cross = false;
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);

@@ -178,6 +178,8 @@ struct BwdParams {
   uint16_t* qs;             // [BH, N, 64] workspace: Q' = bf16(q * log2(e)/8), the forward's operand
   float* lse2;              // [BH, N] workspace: lse * log2(e) (3e38 for an empty row)
   float* delta;             // [BH, N] workspace: rowsum(dout * out)
+  uint2* fold_l;            // [BH, N] workspace: the three bf16 parts of -lse2 (the key walk's fold operand)
+  uint2* fold_d;            // [BH, N] workspace: the three bf16 parts of -delta
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LCV_BSA_ABI_VERSION 10
+#define LCV_BSA_ABI_VERSION 11
 #define LCV_HEAD_DIM 64   /* channels per head (16 + 24 + 24 rotary channels) */
 #define LCV_BLOCK 64      /* tokens per attention block */
 
@@ -245,8 +245,9 @@ lcv_status lcv_qk_rmsnorm_rope3d_backward_noalloc(const void* x, const void* dy,
  *   lse                : fp32 [batch, heads, N], the forward's
  *   dq, dk, dv         : bf16 [batch, heads, N, 64], written completely (fp32 accumulation)
  *   workspace          : fp32 scratch, caller-owned, 16-byte aligned, at least
- *                        lcv_bsa_backward_workspace(batch, heads, N) values (136 B per query
- *                        row: the scaled Q and two per-row terms; -1 for invalid sizes)
+ *                        lcv_bsa_backward_workspace(batch, heads, N) values (152 B per query
+ *                        row: the scaled Q, two per-row terms and their folded bf16 parts;
+ *                        -1 for invalid sizes)
  * Deterministic: every output row is written once, without atomics.  Asynchronous on
  * stream.  Errors: NULL, INVALID_ARG (sizes, alignment, device, small workspace),
  * LAYOUT_MISMATCH (cond_len), UNSUPPORTED (sizes), HIP. */
@@ -287,7 +288,7 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
  *                  get zeros)
  *   workspace    : fp32, caller-owned, 16-byte aligned, at least
  *                  lcv_cross_attention_backward_workspace(batch, heads, n_q, kv_len) values
- *                  (the scaled Q and two per-row terms, 136 B per query row, and the fp32
+ *                  (the scaled Q, two per-row terms and their bf16 parts, 152 B per query row, and the fp32
  *                  partial dK, dV of the query chunks; -1 for invalid sizes)
  * With n_q = 0 (dk = dv = 0) the query-side pointers, with kv_len = 0 (dq = 0) the text-side
  * pointers, and a workspace of size 0 may be NULL.

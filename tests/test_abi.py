@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bsa.lib().lcv_abi_version() == 10
+    assert bsa.lib().lcv_abi_version() == 11
 
 
 QUERY_CASES = [
@@ -122,8 +122,8 @@ def test_cross_attention_argument_errors():
 
 
 def _cross_bwd_workspace(batch, heads, n_q, kv_len):
-    """Expected scratch size: 34 values per query row (the scaled Q as 64 bf16, lse and D;
-    rounded up to 4), then fp32 partial dK and dV per query chunk; chunks give about 512
+    """Expected scratch size: 38 values per query row (the scaled Q as 64 bf16, lse and D, the
+    three bf16 parts of each of those two in 8 bytes; rounded up to 4), then fp32 partial dK and dV per query chunk; chunks give about 512
     key-walk workgroups, at most 64 and at most one per query block, none empty."""
     bh = batch * heads
     nqb, nkb = -(-n_q // 64), -(-kv_len // 64)
@@ -133,7 +133,7 @@ def _cross_bwd_workspace(batch, heads, n_q, kv_len):
         chunks = min(-(-512 // (bh * groups)), 64, nqb)
         per = -(-nqb // chunks)
         chunks = -(-nqb // per)
-    return -(-34 * bh * n_q // 4) * 4 + 2 * chunks * bh * kv_len * 64
+    return -(-38 * bh * n_q // 4) * 4 + 2 * chunks * bh * kv_len * 64
 
 
 def test_cross_backward_workspace_sizes():
@@ -141,7 +141,7 @@ def test_cross_backward_workspace_sizes():
     for args in [(1, 1, 64, 64), (2, 3, 1000, 77), (1, 32, 58560, 512), (4, 2, 0, 512), (1, 1, 100, 0),
                  (3, 5, 4097, 300)]:
         assert f(*args) == _cross_bwd_workspace(*args), args
-    assert f(1, 1, 64, 64) == 34 * 64 + 2 * 64 * 64
+    assert f(1, 1, 64, 64) == 38 * 64 + 2 * 64 * 64
     assert f(0, 1, 64, 64) == -1 and f(1, 1, -1, 64) == -1 and f(1, 1, 64, -1) == -1
 
 
@@ -222,11 +222,12 @@ def test_backward_argument_errors():
 
 
 def test_backward_workspace_sizes():
-    """136 bytes per query row: the scaled Q (64 bf16) and two fp32 per-row terms."""
+    """152 bytes per query row: the scaled Q (64 bf16), two fp32 per-row terms and the three
+    bf16 parts of each of them (8 bytes each)."""
     f = bsa.lib().lcv_bsa_backward_workspace
-    assert f(1, 1, 64) == 34 * 64
-    assert f(1, 32, 86400) == 34 * 32 * 86400
-    assert f(2, 3, 631) == 34 * 6 * 631
+    assert f(1, 1, 64) == 38 * 64
+    assert f(1, 32, 86400) == 38 * 32 * 86400
+    assert f(2, 3, 631) == 38 * 6 * 631
     assert f(0, 1, 64) == -1 and f(1, 0, 64) == -1 and f(1, 1, 0) == -1
 
 
