@@ -350,13 +350,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   // One key block, its halves software-pipelined as in the forward: the second half's S^T
   // and dP^T go to the matrix cores while the vector ALU forms the first half's dS^T, and
   // the first half's dQ^T update runs with the second half's dS^T.
-  auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, auto mask_tag, auto&& copies)
+  // (one body for masked and unmasked blocks: with two instantiations the register allocator
+  // kept the dQ^T accumulators in different registers on the two paths and copied them at
+  // the join, every block)
+  auto block = [&](const unsigned char* kb, const unsigned char* vb, int j, bool masked, auto&& copies)
       __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s0, dp0, s1, dp1;
     bf16x8 d0[2], d1[2];
     sdp_half(kb, vb, 0, s0, dp0);
-    if (MASK) mask_half(j, 0, s0);
+    if (__builtin_expect(masked, 0)) mask_half(j, 0, s0);
     copies();
     sdp_half(kb, vb, 1, s1, dp1);
     ds_half(s0, dp0, d0);
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    if (MASK) mask_half(j, 1, s1);
+    if (__builtin_expect(masked, 0)) mask_half(j, 1, s1);
     dq_half(kb, 0, d0);
     ds_half(s1, dp1, d1);
     // 8 transposing K reads, then the first half's 4 dQ^T MFMAs each followed by vector work
@@ -401,10 +403,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
     if (wave_on && ((ent >> (wave >> 1)) & 1)) {
       const int j = ent >> 8;
       const bool masked = 64 * j + 63 >= key_end || (64 * qblk < P.C && 64 * j + 63 >= P.C);
-      if (masked)
-        block(kc, vc, j, std::true_type{}, copies);
-      else
-        block(kc, vc, j, std::false_type{}, copies);
+      block(kc, vc, j, masked, copies);
     } else {
       copies();
     }
@@ -772,13 +771,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
   // One query block, its halves software-pipelined: the second half's S and dP go to the
   // matrix cores while the vector ALU forms the first half's P and dS, and the first half's
   // dV^T, dK^T updates run with the second half's P and dS.
+  // (one body for masked and unmasked blocks, as in the query walk)
   auto block = [&](const unsigned char* qb, const unsigned char* ob, const uint2* lb, const uint2* db, int i,
-                   auto mask_tag, auto&& copies) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+                   bool masked, auto&& copies) __attribute__((always_inline)) {
     f32x16 s0, dp0, s1, dp1;
     bf16x8 p0[2], d0[2], p1[2], d1[2];
     sdp_half(qb, ob, lb, db, 0, s0, dp0);
-    if (MASK) mask_half(i, 0, s0);
+    if (__builtin_expect(masked, 0)) mask_half(i, 0, s0);
     copies();
     sdp_half(qb, ob, lb, db, 1, s1, dp1);
     pds_half(s0, dp0, p0, d0);
@@ -788,7 +787,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
-    if (MASK) mask_half(i, 1, s1);
+    if (__builtin_expect(masked, 0)) mask_half(i, 1, s1);
     upd_half(qb, ob, 0, p0, d0);
     pds_half(s1, dp1, p1, d1);
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
@@ -819,10 +818,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       const int i = ent >> 8;
       const bool masked = CROSS ? (64 * i + 63 >= P.N || 64 * kblk + 63 >= key_end)
                                 : (64 * i + 63 >= P.N || (64 * i < P.C && 64 * kblk + 63 >= P.C));
-      if (masked)
-        block(qc, oc, lc, dc, i, std::true_type{}, next_copies);
-      else
-        block(qc, oc, lc, dc, i, std::false_type{}, next_copies);
+      block(qc, oc, lc, dc, i, masked, next_copies);
     } else {
       next_copies();
     }
