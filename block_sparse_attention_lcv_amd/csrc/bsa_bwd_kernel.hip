@@ -305,6 +305,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   }
   stage_barrier();
 
+  // the folded lse and D terms do not change along the walk (the wavefront's queries are
+  // fixed): their accumulator tiles are formed once and start every block's products
+  const f32x16 dp_init = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
+  const f32x16 s_init = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
+
   // S^T and dP^T - D of keys 32kt .. 32kt+31 (registers) against the wavefront's queries
   auto sdp_half = [&](const unsigned char* kb, const unsigned char* vb, int kt, f32x16& s, f32x16& dp)
       __attribute__((always_inline)) {
@@ -314,8 +319,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
       ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
       va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
     }
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
+    dp = dp_init;
+    s = s_init;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
