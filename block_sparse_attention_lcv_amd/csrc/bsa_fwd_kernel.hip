@@ -259,16 +259,27 @@ __device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb
 // CROSS: cross-attention of the video queries over text keys/values [BH, kv_len, 64]: every
 // query block attends every text block (dense, no RoPE, no condition rule), keys past the
 // batch item's text length are masked.
-template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const FwdParams P) {
+// The attention walk of one workgroup.  RESIDENT (cross-attention with at most
+// kCrossResidentBlocks text blocks): 2 * kWaves wavefronts hold the head's whole text K and V
+// in LDS, loaded once, and each streams a range of query blocks past it on its own (no
+// copies, no barriers after the load); otherwise kWaves wavefronts walk one workgroup list
+// through a two-stage K/V ring.
+template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS, bool RESIDENT>
+__device__ __forceinline__ void fwd_body(const FwdParams& P) {
   static_assert(!CROSS || (!ROPE_Q && !ROPE_K && !CACHED), "cross-attention has no RoPE and no cache");
+  static_assert(!RESIDENT || CROSS, "only the cross-attention keeps its keys resident");
   // LDS: the K and V tiles of stages 0 and 1 are four separate variables, so the compiler
   // can tell that reads of one stage do not depend on the global -> LDS copies into the
-  // other (with one shared array it makes those reads wait for every copy in flight).
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
+  // other (with one shared array it makes those reads wait for every copy in flight).  The
+  // resident walk keeps the K and V tiles of text block j at tiles 2j and 2j + 1 of lds_k0,
+  // so that the lane offsets carry the block and the tile bases fit the LDS instructions'
+  // immediate offsets.
+  constexpr int kBytes0 = RESIDENT ? 2 * kCrossResidentBlocks * kTileBytes : kTileBytes;
+  constexpr int kBytes1 = RESIDENT ? 16 : kTileBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kBytes0];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kBytes1];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kBytes1];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kBytes1];
   // cos/sin table of the fused RoPE (its own variable, so that the compiler can tell its
   // writes apart from the copies into the stages)
   __shared__ __attribute__((aligned(16))) float2 lds_tab[(ROPE_Q || ROPE_K) ? kMaxRopeEntries : 1];
@@ -284,6 +295,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   // layout's work order (longest first, in runs of consecutive lists).  The hardware starts
   // each workgroup as a slot frees up, so the longest lists of a head go first and the
   // shortest fill the end.
+  // The resident walk's items are (batch, head, range of q_per_part query blocks), the
+  // ranges counted by n_st_active.
   const int per_xcd = (int)(gridDim.x >> 3);
   const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (item >= P.n_items) return;
@@ -322,7 +335,19 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 #pragma unroll
   for (int c = 0; c < kLoadsPerWave; ++c) voff[c] = stage_lane_offset(wave, lane, c);
   int ent_cur = 0, ent_next = 0;
-  if (cnt > 0) {
+  if constexpr (RESIDENT) {
+    // every text block: wavefront w issues wave-load w of each tile (8 rows), rows past the
+    // text read zeros
+    const uint32_t off = stage_lane_offset(wave >> 1, lane, wave & 1);
+    for (int j = 0; j < cnt; ++j) {
+      const int rows = key_end - 64 * j < 64 ? key_end - 64 * j : 64;
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kvs.k_noise + (uint64_t)j * kTileBytes, rows);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(kvs.v_noise + (uint64_t)j * kTileBytes, rows);
+      unsigned char* kt = lds_k0 + 2 * j * kTileBytes + 1024 * wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)kt, 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(kt + kTileBytes), 16, off, 0, 0, 0);
+    }
+  } else if (cnt > 0) {
     ent_cur = __builtin_amdgcn_readfirstlane(entry(0));
     if (cnt > 1) ent_next = __builtin_amdgcn_readfirstlane(entry(1));
     const int j0 = ent_cur >> 8;
@@ -331,23 +356,37 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 
   // ---- this wavefront's query block as MFMA B operands: qf[qt][ks] holds rows
   // 32*qt + (lane & 31), channels 16*ks + 8*(lane >> 5) .. +7, scaled by log2(e)/8
-  const int qblk = st * kWaves + wave;
-  const bool wave_on = (qblk < P.n_blocks) && (64 * qblk + 63 >= P.q_row0) && (64 * qblk < P.q_end);
+  int qblk = 0;
+  bool wave_on = false;
   bf16x8 qf[2][4];
   int qtok[2];
   bool qok[2];
+  // the rows of query block qb this lane owns, and whether they are computed
+  auto query_rows = [&](int qb) __attribute__((always_inline)) {
+    qblk = qb;
+    wave_on = (qb < P.n_blocks) && (64 * qb + 63 >= P.q_row0) && (64 * qb < P.q_end);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      qtok[qt] = 64 * qb + 32 * qt + l32;
+      qok[qt] = wave_on && qtok[qt] >= P.q_row0 && qtok[qt] < P.q_end;
+    }
+  };
   // all eight 16-byte loads go out before any is used (rows outside the call's range read a
   // valid row of the tensor and are zeroed afterwards), so the block costs one memory latency
   u32x4 qraw[2][4];
+  auto load_query = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    qtok[qt] = 64 * qblk + 32 * qt + l32;
-    qok[qt] = wave_on && qtok[qt] >= P.q_row0 && qtok[qt] < P.q_end;
-    int qr = qtok[qt] - P.q_row0;
-    qr = qr < 0 ? 0 : (qr < P.q_rows ? qr : P.q_rows - 1);
-    const uint16_t* qrow = P.q + ((int64_t)bh * P.q_rows + qr) * 64;
+    for (int qt = 0; qt < 2; ++qt) {
+      int qr = 64 * qb + 32 * qt + l32 - P.q_row0;
+      qr = qr < 0 ? 0 : (qr < P.q_rows ? qr : P.q_rows - 1);
+      const uint16_t* qrow = P.q + ((int64_t)bh * P.q_rows + qr) * 64;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qraw[qt][ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * ks + g));
+      for (int ks = 0; ks < 4; ++ks) qraw[qt][ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * ks + g));
+    }
+  };
+  if constexpr (!RESIDENT) {
+    query_rows(st * kWaves + wave);
+    load_query(st * kWaves + wave);
   }
   // ---- cos/sin table of every (axis, position, pair) of the grid
   float2* tab = lds_tab;
@@ -374,20 +413,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   }
 
   // rotation (fused Q RoPE) and scaling of the loaded query block
+  auto query_operands = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    Coords xyz{0u, 0u, 0u};
-    if (ROPE_Q && qok[qt]) xyz = token_coords((uint32_t)qtok[qt], P);
+    for (int qt = 0; qt < 2; ++qt) {
+      Coords xyz{0u, 0u, 0u};
+      if (ROPE_Q && qok[qt]) xyz = token_coords((uint32_t)qtok[qt], P);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c = 2 * ks + g;
-      u32x4 raw = qraw[qt][ks];
-      if constexpr (ROPE_Q) raw = rope_chunk(raw, c, xyz, tab, P);
-      raw = scale_chunk_log2(raw);
-      if (!qok[qt]) raw = u32x4{0u, 0u, 0u, 0u};
-      qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = 2 * ks + g;
+        u32x4 raw = qraw[qt][ks];
+        if constexpr (ROPE_Q) raw = rope_chunk(raw, c, xyz, tab, P);
+        raw = scale_chunk_log2(raw);
+        if (!qok[qt]) raw = u32x4{0u, 0u, 0u, 0u};
+        qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
+      }
     }
-  }
+  };
+  if constexpr (!RESIDENT) query_operands();
 
   // ---- per-lane LDS offsets (stage, 32-row and 16-row steps become immediates)
   uint32_t ka_off[4];
@@ -403,17 +445,33 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     vb_off_hi[dt] = tile_off(krow0 + 8, dcol >> 3) + (uint32_t)(lane & 1) * 8u;
   }
 
+  auto shift_offsets = [&](int bytes) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka_off[ks] += (uint32_t)bytes;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      vb_off[dt] += (uint32_t)bytes;
+      vb_off_hi[dt] += (uint32_t)bytes;
+    }
+  };
+
   // ---- state
   f32x16 o[2][2];   // O^T tiles [d tile][query tile]
+  float mref[2];    // reference of each row (log2 units), -inf = none yet
+  float lsum[2];
+  bool ref_nonzero;  // some row of the wavefront has a reference other than 0
+  auto clear_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[a][b][r] = 0.f;
-  float mref[2] = {-INFINITY, -INFINITY};   // reference of each row (log2 units), -inf = none yet
-  float lsum[2] = {0.f, 0.f};
-  bool ref_nonzero = false;                 // some row of the wavefront has a reference other than 0
+        for (int r = 0; r < 16; ++r) o[a][b][r] = 0.f;
+    mref[0] = mref[1] = -INFINITY;
+    lsum[0] = lsum[1] = 0.f;
+    ref_nonzero = false;
+  };
+  clear_state();
 
   // the first block's K rotated into its stage (fused K RoPE), then every copy of it landed
   if constexpr (ROPE_K) {
@@ -424,8 +482,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 
   // S^T[key][query] = K Q'^T for the keys 32*kt .. 32*kt+31 of a stage: the K operands, then
   // the products
-  auto read_k = [&](auto stage_tag, int kt, bf16x8 (&ka)[4]) {
-    const unsigned char* kb = decltype(stage_tag)::value ? lds_k1 : lds_k0;
+  auto read_k = [&](const unsigned char* kb, int kt, bf16x8 (&ka)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
@@ -463,7 +520,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = key < key_end && (qtok[qt] >= P.C || key < P.C);
+        const bool ok = key < key_end && (CROSS || qtok[qt] >= P.C || key < P.C);
         if (!ok) s[qt][r] = -INFINITY;
       }
   };
@@ -509,8 +566,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
 
   // O^T[d][query] += V^T P^T over the two 16-key steps of half kt; V^T operands by
   // transposing reads of the row-major V tile
-  auto pv_half = [&](auto stage_tag, int kt, const bf16x8 (&pb)[2][2]) {
-    const unsigned char* vb = decltype(stage_tag)::value ? lds_v1 : lds_v0;
+  auto pv_half = [&](const unsigned char* vb, int kt, const bf16x8 (&pb)[2][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t js_off = 2048u * (2 * kt + h);
@@ -532,17 +588,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
   // with the first half's softmax and the first half's P V with the second half's softmax,
   // interleaved instruction by instruction.  Each half's scores are taken relative to the
   // references as they stand when its softmax starts (after the first half's rescale, if any).
-  auto attend = [&](auto stage_tag, auto mask_tag, int j, auto&& copies) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto attend = [&](const unsigned char* kb, const unsigned char* vb, auto mask_tag, int j, auto&& copies) {
+    // the mask choice: a compile-time tag (two instantiations of the body), or a runtime
+    // flag (one body for masked and unmasked blocks)
+    bool MASK;
+    if constexpr (std::is_same_v<decltype(mask_tag), bool>)
+      MASK = __builtin_expect(mask_tag, false);
+    else
+      MASK = decltype(mask_tag)::value;
     const int key0 = 64 * j;
     f32x16 s0[2], s1[2];
     bf16x8 p0[2][2], p1[2][2];
     float psum[2], delta[2];
     bool trig[2];
     bf16x8 ka0[4], ka1[4];
-    read_k(stage_tag, 0, ka0);
+    read_k(kb, 0, ka0);
     qk_half(ka0, s0);
-    read_k(stage_tag, 1, ka1);
+    read_k(kb, 1, ka1);
     // the next block's copies go out under the first half's matrix-core work, so that the
     // loads of all wavefronts do not queue up at the start of the step
     copies();
@@ -565,7 +627,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     lsum[1] += psum[1];
     if (MASK) mask_half(key0, 1, s1);
     rebase(s1);
-    pv_half(stage_tag, 0, p0);
+    pv_half(vb, 0, p0);
     softmax_fast(s1, p1, psum, trig);
     // 8 V^T reads, then the first half's 8 P V MFMAs each followed by vector work of the
     // second half's softmax
@@ -578,7 +640,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s1, p1, psum, trig, delta);
     lsum[0] += psum[0];
     lsum[1] += psum[1];
-    pv_half(stage_tag, 1, p1);
+    pv_half(vb, 1, p1);
   };
 
   auto step = [&](auto stage_tag, int e) {
@@ -599,10 +661,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
       // same in every variant because the register allocation of the cached one spilled
       // inside the loop without it)
       const bool need_mask = 64 * j + 63 >= key_end || (64 * qblk < P.C && 64 * j + 63 >= P.C);
+      const unsigned char* kb = STAGE ? lds_k1 : lds_k0;
+      const unsigned char* vb = STAGE ? lds_v1 : lds_v0;
       if (__builtin_expect(need_mask, 0))
-        attend(stage_tag, std::true_type{}, j, copies);
+        attend(kb, vb, std::true_type{}, j, copies);
       else
-        attend(stage_tag, std::false_type{}, j, copies);
+        attend(kb, vb, std::false_type{}, j, copies);
     } else {
       copies();
     }
@@ -613,36 +677,75 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const 
     ent_next = __builtin_amdgcn_readfirstlane(ent_after_raw);
   };
 
-  int e = 0;
-  for (; e + 1 < cnt; e += 2) {
-    step(std::integral_constant<int, 0>{}, e);
-    step(std::integral_constant<int, 1>{}, e + 1);
-  }
-  if (e < cnt) step(std::integral_constant<int, 0>{}, e);
-
   // ---- epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2
-  if (wave_on) {
+  auto store_output = [&]() __attribute__((always_inline)) {
+    if (wave_on) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float lt = lsum[qt] + partner(lsum[qt]);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      if (qok[qt]) {
-        const int64_t row = (int64_t)bh * P.q_rows + (qtok[qt] - P.q_row0);
-        uint16_t* orow = P.out + row * 64;
+      for (int qt = 0; qt < 2; ++qt) {
+        const float lt = lsum[qt] + partner(lsum[qt]);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (qok[qt]) {
+          const int64_t row = (int64_t)bh * P.q_rows + (qtok[qt] - P.q_row0);
+          uint16_t* orow = P.out + row * 64;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+          for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-          for (int R = 0; R < 4; ++R) {
-            const int d = 32 * dt + 8 * R + 4 * g;
-            uint2 pk;
-            pk.x = pack_bf16x2(o[dt][qt][4 * R] * inv, o[dt][qt][4 * R + 1] * inv);
-            pk.y = pack_bf16x2(o[dt][qt][4 * R + 2] * inv, o[dt][qt][4 * R + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + d) = pk;
-          }
-        if (P.lse != nullptr && g == 0) P.lse[row] = lt > 0.f ? (mref[qt] + log2f(lt)) * kLn2 : -INFINITY;
+            for (int R = 0; R < 4; ++R) {
+              const int d = 32 * dt + 8 * R + 4 * g;
+              uint2 pk;
+              pk.x = pack_bf16x2(o[dt][qt][4 * R] * inv, o[dt][qt][4 * R + 1] * inv);
+              pk.y = pack_bf16x2(o[dt][qt][4 * R + 2] * inv, o[dt][qt][4 * R + 3] * inv);
+              *reinterpret_cast<uint2*>(orow + d) = pk;
+            }
+          if (P.lse != nullptr && g == 0) P.lse[row] = lt > 0.f ? (mref[qt] + log2f(lt)) * kLn2 : -INFINITY;
+        }
       }
     }
+  };
+
+  if constexpr (RESIDENT) {
+    // query blocks [blk0, blk1) of the head, wavefront w taking blk0 + w, blk0 + w + 2 kWaves,
+    // ...; the next block's rows are loaded before this block's output is stored
+    const int blk0 = level * P.q_per_part;
+    const int blk1 = blk0 + P.q_per_part < P.n_blocks ? blk0 + P.q_per_part : P.n_blocks;
+    int qb = blk0 + wave;
+    if (qb < blk1) load_query(qb);
+    auto no_copies = []() {};
+    while (qb < blk1) {
+      query_rows(qb);
+      query_operands();
+      // the lane offsets step through the text blocks and are set back afterwards
+      for (int j = 0; j < cnt; ++j) {
+        attend(lds_k0, lds_k0 + kTileBytes, 64 * j + 63 >= key_end, j, no_copies);
+        shift_offsets(2 * kTileBytes);
+      }
+      shift_offsets(-2 * kTileBytes * cnt);
+      const int qn = qb + 2 * kWaves;
+      if (qn < blk1) load_query(qn);
+      store_output();
+      clear_state();
+      qb = qn;
+    }
+  } else {
+    int e = 0;
+    for (; e + 1 < cnt; e += 2) {
+      step(std::integral_constant<int, 0>{}, e);
+      step(std::integral_constant<int, 1>{}, e + 1);
+    }
+    if (e < cnt) step(std::integral_constant<int, 0>{}, e);
+    store_output();
   }
+}
+
+template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS>
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void bsa_fwd_kernel(const FwdParams P) {
+  fwd_body<ROPE_Q, ROPE_K, CACHED, CROSS, false>(P);
+}
+
+// Cross-attention over at most kCrossResidentBlocks text blocks: one workgroup of
+// 2 * kWaves wavefronts per compute unit (the text takes 128 KB of LDS).
+__global__ __launch_bounds__(2 * kThreads, kWavesPerSimd) void bsa_cross_resident_kernel(const FwdParams P) {
+  fwd_body<false, false, false, true, true>(P);
 }
 
 template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS = false>
@@ -676,6 +779,10 @@ hipError_t launch_bsa_fwd(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_cross_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.n_items == 0) return hipSuccess;
   const unsigned groups = item_groups(p.n_items);
+  if (p.q_per_part > 0) {   // the text fits in LDS
+    hipLaunchKernelGGL(bsa_cross_resident_kernel, dim3(groups), dim3(2 * kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   return launch_variant<false, false, false, true>(p, groups, 0, stream);
 }
 

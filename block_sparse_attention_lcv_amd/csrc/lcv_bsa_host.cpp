@@ -232,6 +232,11 @@ constexpr int64_t kBwdRowFloats = 38;
 // workgroup; the key walk takes four text blocks and one chunk of the query blocks, with
 // enough chunks to give the chip about 512 workgroups; the chunks' fp32 partial dK, dV
 // follow the per-row values in the workspace (16-byte aligned).
+// workgroups the cross-attention forward with the text in LDS aims for (one per compute unit)
+#ifndef LCV_CROSS_FWD_WORKGROUPS
+#define LCV_CROSS_FWD_WORKGROUPS 256
+#endif
+
 // workgroups the two walks of the cross-attention backward aim for (a few per compute unit)
 #ifndef LCV_CROSS_KEY_WALK_WORKGROUPS
 #define LCV_CROSS_KEY_WALK_WORKGROUPS 512
@@ -570,6 +575,20 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
   p.kv_len = kv_len;
   p.kv_lens = kv_lens;
   p.heads = heads;
+  // With at most kCrossResidentBlocks text blocks the text stays in LDS: about
+  // LCV_CROSS_FWD_WORKGROUPS workgroups (one per compute unit), each streaming a range of
+  // query blocks (a multiple of its 2 * kWaves wavefronts) past its head's text.
+  if ((int64_t)kv_len <= (int64_t)lcv::kCrossResidentBlocks * 64) {
+    constexpr int64_t kRound = 2 * lcv::kWaves;
+    const int64_t rounds = (n_blocks + kRound - 1) / kRound;
+    int64_t parts = (LCV_CROSS_FWD_WORKGROUPS + bh - 1) / bh;
+    parts = parts < rounds ? parts : rounds;
+    const int64_t per = ((n_blocks + parts - 1) / parts + kRound - 1) / kRound * kRound;
+    parts = (n_blocks + per - 1) / per;
+    p.q_per_part = (int32_t)per;
+    p.n_st_active = (int32_t)parts;
+    p.n_items = (int32_t)(bh * parts);
+  }
   hipError_t e = lcv::launch_cross_fwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "cross-attention launch");
   return ok();

@@ -166,6 +166,8 @@ struct FwdParams {
   int32_t kv_len;
   const int32_t* kv_lens;   // [B] device, or nullptr (all kv_len)
   int32_t heads;
+  int32_t q_per_part;       // > 0: query blocks per workgroup of the walk with the text in LDS
+                            // (a multiple of 2 * kWaves; n_st_active counts the ranges)
 };
 
 struct BwdParams {

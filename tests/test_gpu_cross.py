@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from lcv_inputs import TEXT_LEN, WORKLOADS, bf16_bits_to_f64, qkv_bits, text_kv_bits
-from tests.gpu_util import assert_lse_close, assert_out_close, from_dev_f64, say, to_dev
+from tests.gpu_util import assert_lse_close, assert_out_close, from_dev_f64, lse_error_budget, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -94,3 +94,45 @@ def test_cross_workload_sampled_rows(lib):
                                           rows=rows)
     assert_out_close(from_dev_f64(out[:, :, idx]), ref_o, "t2v720 cross")
     assert_lse_close(lse[:, :, idx].cpu().numpy().astype(np.float64), ref_l, "t2v720 cross")
+
+
+def _bf16(x: float) -> np.uint16:
+    return np.uint16(np.float32(x).view(np.uint32) >> 16)   # the values used here are exact in bf16
+
+
+@pytest.mark.parametrize("text_len", [307, 700], ids=["text-in-lds", "text-streamed"])
+def test_cross_reference_moves(lib, text_len):
+    """Text blocks whose scores lie far apart: channel 0 of the keys is constant per 64-key
+    block (2, 6, -30, 0, 3, repeated) and channel 0 of the queries cycles through 0, 64, -64,
+    16, -256 and 128, so a row's blocks are shifted against each other by up to ~1,000
+    (natural units).  This walks the transitions of the lazy row reference: rows whose
+    reference stays 0 (0, 16), rows that move it up in a later block by a large step (64),
+    past an fp32 overflow of the exponentials (-64: scores ~346 in log2 units against the
+    reference 0), and rows whose first block sets it far below (-256) or above (128) zero and
+    a later block moves it up again.  Outputs against the oracle at the usual bounds; the LSE within
+    the worst case of its score arithmetic (lse_error_budget: the one bf16 rounding of the
+    query operand moves the dominant block's shift by up to 2^-8 of itself).  307 text tokens
+    stay in LDS (the last block partly masked), 700 are streamed."""
+    batch, heads, n_q = 1, 2, 390
+    say(f"[cross] reference moves L={text_len}")
+    qb, _, _ = qkv_bits(57, batch, heads, n_q)
+    kb, vb = text_kv_bits(57, batch, heads, text_len)
+    qb, kb = qb.copy(), kb.copy()
+    q0 = [0.0, 64.0, -64.0, 16.0, -256.0, 128.0]
+    k0 = [2.0, 6.0, -30.0, 0.0, 3.0]
+    for r in range(n_q):
+        qb[:, :, r, 0] = _bf16(q0[r % len(q0)])
+    for key in range(text_len):
+        kb[:, :, key, 0] = _bf16(k0[(key // 64) % len(k0)])
+    out, lse = lib.cross_attention(to_dev(qb), to_dev(kb), to_dev(vb))
+    _sync()
+    qf, kf, vf = bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+    ref_o, ref_l = oracle.cross_attention(qf, kf, vf)
+    assert_out_close(from_dev_f64(out), ref_o, f"reference moves L={text_len}")
+    got_l = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_l))
+    mask = np.ones((n_q, text_len), dtype=bool)
+    for h in range(heads):
+        worst, _ = lse_error_budget(qf[0, h], kf[0, h], mask, ref_l[0, h], rope=False)
+        err = np.abs(got_l[0, h] - ref_l[0, h])
+        assert np.all(err <= worst), f"L={text_len} head {h}: lse error {float(np.max(err - worst)):.3e} above its bound"
