@@ -256,14 +256,14 @@ __device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb
   return acc0 + acc1;
 }
 
-// CROSS: cross-attention of the video queries over text keys/values [BH, kv_len, 64]: every
-// query block attends every text block (dense, no RoPE, no condition rule), keys past the
-// batch item's text length are masked.
-// The attention walk of one workgroup.  RESIDENT (cross-attention with at most
-// kCrossResidentBlocks text blocks): 2 * kWaves wavefronts hold the head's whole text K and V
-// in LDS, loaded once, and each streams a range of query blocks past it on its own (no
-// copies, no barriers after the load); otherwise kWaves wavefronts walk one workgroup list
-// through a two-stage K/V ring.
+// The attention walk of one workgroup.  CROSS: cross-attention of the video queries over
+// text keys/values [BH, kv_len, 64]: every query block attends every text block (dense, no
+// RoPE, no condition rule), keys past the batch item's text length are masked.  RESIDENT
+// (cross-attention with at most kCrossResidentBlocks text blocks): 2 * kWaves wavefronts
+// hold the head's whole text K and V in LDS, loaded once, and each streams a range of query
+// blocks past it on its own (no copies, no barriers after the load); otherwise kWaves
+// wavefronts walk one workgroup list (or, CROSS, every text block) through a two-stage K/V
+// ring.
 template <bool ROPE_Q, bool ROPE_K, bool CACHED, bool CROSS, bool RESIDENT>
 __device__ __forceinline__ void fwd_body(const FwdParams& P) {
   static_assert(!CROSS || (!ROPE_Q && !ROPE_K && !CACHED), "cross-attention has no RoPE and no cache");
@@ -591,11 +591,11 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
   auto attend = [&](const unsigned char* kb, const unsigned char* vb, auto mask_tag, int j, auto&& copies) {
     // the mask choice: a compile-time tag (two instantiations of the body), or a runtime
     // flag (one body for masked and unmasked blocks)
-    bool MASK;
+    bool masked;
     if constexpr (std::is_same_v<decltype(mask_tag), bool>)
-      MASK = __builtin_expect(mask_tag, false);
+      masked = __builtin_expect(mask_tag, false);
     else
-      MASK = decltype(mask_tag)::value;
+      masked = decltype(mask_tag)::value;
     const int key0 = 64 * j;
     f32x16 s0[2], s1[2];
     bf16x8 p0[2][2], p1[2][2];
@@ -612,7 +612,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    if (MASK) mask_half(key0, 0, s0);
+    if (masked) mask_half(key0, 0, s0);
     rebase(s0);
     qk_half(ka1, s1);
     softmax_fast(s0, p0, psum, trig);
@@ -625,7 +625,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
     if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s0, p0, psum, trig, delta);
     lsum[0] += psum[0];
     lsum[1] += psum[1];
-    if (MASK) mask_half(key0, 1, s1);
+    if (masked) mask_half(key0, 1, s1);
     rebase(s1);
     pv_half(vb, 0, p0);
     softmax_fast(s1, p1, psum, trig);
