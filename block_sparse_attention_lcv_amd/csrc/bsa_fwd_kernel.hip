@@ -24,9 +24,10 @@
 //    block's probabilities grow too large (lazy rescaling), and then to a multiple of 64,
 //    so that it stays 0 for rows whose scores stay near 0; a wavefront with some nonzero
 //    reference subtracts it from its scores with the vector ALU.  The common score costs one
-//    v_exp_f32, half a conversion and half a dot2.  Each row's decisions depend on that row
-//    alone, so results do not depend on which other rows share the wavefront (the cached
-//    call reproduces the full call bit for bit).
+//    v_exp_f32 and half a conversion on the vector ALU; the row sums of the probabilities
+//    are products on the matrix cores (a 0/1 selection operand against the P operands).
+//    Each row's decisions depend on that row alone, so results do not depend on which other
+//    rows share the wavefront (the cached call reproduces the full call bit for bit).
 //  * O^T += V^T P^T with the same MFMA: P (bf16) comes straight from the S^T registers, V^T
 //    operands come from the row-major V tile through ds_read_b64_tr_b16 transposing reads.
 //  * Workgroups are numbered so that each XCD (blockIdx % 8 on MI355X) receives a
@@ -47,17 +48,26 @@ constexpr int kThreads = 64 * kWaves;
 #define LCV_WAVES_PER_SIMD 2
 #endif
 constexpr int kWavesPerSimd = LCV_WAVES_PER_SIMD;  // occupancy the register budget is sized for
-// Lazy rescaling with a coarse reference.  A row's reference moves only when a lane's
-// probabilities in one 32-key half (16 keys of its row) sum past 2^40, and then to the
-// multiple of 64 nearest the row's largest score, which so lies within 32 of it (a row's
-// first block always sets it).  Every probability therefore stays below 2^40 and a row's sum
-// below 2^56, far inside fp32 and bf16, the largest probability of a row is at least 2^-32,
-// and a rescale multiplies by an exact power of two.  Testing each lane on its own keeps the
-// partner exchange out of the common path.
+// Lazy rescaling with a coarse reference.  A row's reference moves only when its
+// probabilities in one 32-key half sum past 2^40, and then to the multiple of 64 nearest the
+// row's largest score, which so lies within 32 of it (a row's first block always sets it).
+// Every probability therefore stays below 2^40 and a row's sum below 2^56, far inside fp32
+// and bf16, the largest probability of a row is at least 2^-32, and a rescale multiplies by
+// an exact power of two.  Both lanes of a row get the row's half sum from the matrix cores
+// (half_row_sum), so the test needs no partner exchange.
 constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
+
+// Vector instructions of a half's softmax placed after each of the 8 MFMAs it is interleaved
+// with (about 52 per half: 32 exponentials, 16 conversions, the tests)
+#ifndef LCV_VALU_PER_MFMA
+#define LCV_VALU_PER_MFMA 6
+#endif
+constexpr int kValuPerMfma = LCV_VALU_PER_MFMA;
 __device__ __forceinline__ float coarse_ref(float m) { return 64.0f * __builtin_rintf(m * (1.0f / 64.0f)); }
 
 __device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Coords {
   uint32_t t, y, x;
@@ -225,14 +235,10 @@ __device__ __forceinline__ void stage_store_k(const FwdParams& P, unsigned char*
 
 // p = 2^(s + shift) for the 16 scores of query tile qt held by this lane in one 32-key half
 // (the scores already taken relative to the row's reference m), packed to bf16 as the B
-// operands of the two 16-key P*V steps; returns the lane's sum of the rounded
-// probabilities.  The bf16 pairs are built as bf16x2 values and fed to the dot2 intrinsic
-// directly: taking them out of a u32 vector by bit_cast was mis-optimised by the compiler
-// into reusing one pair for several dot2 operands.
+// operands of the two 16-key P*V steps: pb[h] holds keys 16h + 8(lane/32) .. +7 of query
+// lane % 32.
 template <bool SHIFT>
-__device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb)[2]) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float acc0 = 0.f, acc1 = 0.f;
+__device__ __forceinline__ void probs(const f32x16& s, float shift, bf16x8 (&pb)[2]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     bf16x2 w[4];
@@ -246,14 +252,32 @@ __device__ __forceinline__ float probs(const f32x16& s, float shift, bf16x8 (&pb
       const f32x2_t p = {__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1)};
       w[e2] = __builtin_convertvector(p, bf16x2);
     }
-    acc0 = __builtin_amdgcn_fdot2_f32_bf16(w[0], ones, acc0, false);
-    acc1 = __builtin_amdgcn_fdot2_f32_bf16(w[1], ones, acc1, false);
-    acc0 = __builtin_amdgcn_fdot2_f32_bf16(w[2], ones, acc0, false);
-    acc1 = __builtin_amdgcn_fdot2_f32_bf16(w[3], ones, acc1, false);
     pb[h] = __builtin_shufflevector(__builtin_shufflevector(w[0], w[1], 0, 1, 2, 3),
                                     __builtin_shufflevector(w[2], w[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  return acc0 + acc1;
+}
+
+// The 0/1 operand of half_row_sum: lane l supplies row l % 16, keys-group l / 16 of the
+// 16 x 32 A operand of v_mfma_f32_16x16x32_bf16, and a row of even (odd) index selects the
+// key groups of even (odd) index.
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+  const uint32_t one2 = 0x3F803F80u;   // two bf16 ones
+  const uint32_t v = ((lane & 1) == ((lane >> 4) & 1)) ? one2 : 0u;
+  return __builtin_bit_cast(bf16x8, u32x4{v, v, v, v});
+}
+
+// Sum of the rounded probabilities of one 32-key half for the lane's query row, on the
+// matrix cores.  Read as the B operand of v_mfma_f32_16x16x32_bf16 (lane l: column l % 16,
+// key group l / 16), pb[h] holds query n = l % 16 in groups 0 and 2 (keys 0-7 and 8-15 of
+// the step) and query n + 16 in groups 1 and 3; so with the selector as A, result rows of even
+// index hold the sum of query l % 16 over both steps and odd rows that of query l % 16 + 16.
+// Lane l reads its own query l % 32 from result row 0 (l % 32 < 16, upper = false) or 1.
+// Both lanes of a query read the same sum.
+__device__ __forceinline__ float half_row_sum(const bf16x8 (&pb)[2], const bf16x8& sel, bool upper) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[1], acc, 0, 0, 0);
+  return upper ? acc[1] : acc[0];
 }
 
 // The attention walk of one workgroup.  CROSS: cross-attention of the video queries over
@@ -456,6 +480,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
   };
 
   // ---- state
+  const bf16x8 sum_sel = row_sum_selector(lane);   // operand and result row of half_row_sum
+  const bool sum_upper = (lane & 16) != 0;
   f32x16 o[2][2];   // O^T tiles [d tile][query tile]
   float mref[2];    // reference of each row (log2 units), -inf = none yet
   float lsum[2];
@@ -526,14 +552,15 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
   };
 
   // Online softmax of one half: p = 2^(s - m) with the scores s already taken relative to
-  // the row's reference m.  The reference only moves when a lane's probabilities in this half
-  // exceed the limit; the fast path is then one v_exp_f32, half a conversion and half a dot2
-  // per score.  The slow path recomputes the half's probabilities against the moved
+  // the row's reference m.  The reference only moves when the row's probabilities in this half
+  // exceed the limit; the fast path is then one v_exp_f32 and half a conversion per score on
+  // the vector ALU, and four small products for the row sums.  The slow path recomputes the half's probabilities against the moved
   // reference (shifted by its change, delta).
   auto softmax_fast = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float (&psum)[2], bool (&trig)[2]) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      psum[qt] = probs<false>(s[qt], 0.f, pb[qt]);
+      probs<false>(s[qt], 0.f, pb[qt]);
+      psum[qt] = half_row_sum(pb[qt], sum_sel, sum_upper);
       trig[qt] = (mref[qt] == -INFINITY) || !(psum[qt] <= kRescaleLimit);
     }
   };
@@ -559,7 +586,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
       mref[qt] = m_new;
       const float m_base_new = (m_new == -INFINITY) ? 0.f : m_new;
       delta[qt] = m_base - m_base_new;
-      psum[qt] = probs<true>(s[qt], delta[qt], pb[qt]);
+      probs<true>(s[qt], delta[qt], pb[qt]);
+      psum[qt] = half_row_sum(pb[qt], sum_sel, sum_upper);
     }
     ref_nonzero = __any((mref[0] != 0.f && mref[0] != -INFINITY) || (mref[1] != 0.f && mref[1] != -INFINITY));
   };
@@ -620,7 +648,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
     if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s0, p0, psum, trig, delta);
     lsum[0] += psum[0];
@@ -635,7 +663,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
     if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s1, p1, psum, trig, delta);
     lsum[0] += psum[0];
@@ -682,7 +710,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
     if (wave_on) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        const float lt = lsum[qt] + partner(lsum[qt]);
+        const float lt = lsum[qt];   // the row's sum (both lanes of a row hold it)
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (qok[qt]) {
           const int64_t row = (int64_t)bh * P.q_rows + (qtok[qt] - P.q_row0);
