@@ -83,6 +83,24 @@ __device__ __forceinline__ bf16x8 ones_slots(int g) {
   return g == 0 ? bf16x8{one, one, one, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
 }
 
+// A fold step on the 32x32x8 product, which covers the three parts at half the cycles of
+// the 32x32x16 one.  Its 4-wide operands: lane l holds slots k = 4 (l / 32) .. +3 of its row
+// (A) or column (B); the parts sit in slots 0-2 of the lanes with l / 32 = 0 and meet ones
+// there.  fold_rows: the parts of row l % 32 as A (result rows = the folded rows);
+// fold_cols: as B (result columns).
+__device__ __forceinline__ i16x4 fold4(uint2 parts, int g) {
+  return __builtin_bit_cast(i16x4, uint2{g == 0 ? parts.x : 0u, g == 0 ? parts.y : 0u});
+}
+__device__ __forceinline__ i16x4 ones4(int g) {
+  return __builtin_bit_cast(i16x4, uint2{g == 0 ? 0x3F803F80u : 0u, g == 0 ? 0x00003F80u : 0u});
+}
+__device__ __forceinline__ f32x16 fold_rows(uint2 parts, int g) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fold4(parts, g), ones4(g), f32x16{}, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 fold_cols(uint2 parts, int g) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones4(g), fold4(parts, g), f32x16{}, 0, 0, 0);
+}
+
 // 8 channels (chunk c) of row `row` of a [rows, 64] bf16 tensor as an MFMA operand; zero
 // when !ok.
 __device__ __forceinline__ bf16x8 load_chunk(const uint16_t* base, int64_t row, int c, bool ok) {
@@ -478,7 +496,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const bf16x8 ones = ones_slots(g);
   uint32_t ka_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
@@ -515,8 +532,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     const int qnext = qblk + kWaves;
 
     const int q = 64 * qblk + 32 * (wave & 1) + l32;
-    const bf16x8 fold_l = fold_neg(lse2, g);
-    const bf16x8 fold_d = fold_neg(dlt, g);
+    const uint2 fold_l = fold_parts(lse2);
+    const uint2 fold_d = fold_parts(dlt);
     f32x16 dqt[2];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -531,8 +548,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
         ka[ks] = *reinterpret_cast<const bf16x8*>(kb + ka_off[ks] + 4096u * kt);
         va[ks] = *reinterpret_cast<const bf16x8*>(vb + ka_off[ks] + 4096u * kt);
       }
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_d, f32x16{}, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, fold_l, f32x16{}, 0, 0, 0);
+      dp = fold_cols(fold_d, g);
+      s = fold_cols(fold_l, g);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
@@ -669,7 +686,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     kf[ks] = load_chunk(P.k + kv_base * 64, key, 2 * ks + g, kok);
     vf[ks] = load_chunk(P.v + kv_base * 64, key, 2 * ks + g, kok);
   }
-  const bf16x8 ones = ones_slots(g);
   uint32_t qa_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qa_off[ks] = tile_off(l32, 2 * ks + g);
@@ -730,10 +746,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       qa[ks] = *reinterpret_cast<const bf16x8*>(qb + qa_off[ks] + 4096u * qt);
       oa[ks] = *reinterpret_cast<const bf16x8*>(ob + qa_off[ks] + 4096u * qt);
     }
-    const bf16x8 fold_l = fold_operand(lb[32 * qt + l32], g);
-    const bf16x8 fold_d = fold_operand(db[32 * qt + l32], g);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_l, ones, f32x16{}, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_d, ones, f32x16{}, 0, 0, 0);
+    s = fold_rows(lb[32 * qt + l32], g);
+    dp = fold_rows(db[32 * qt + l32], g);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
