@@ -65,7 +65,7 @@ typedef enum lcv_status {
   LCV_ERR_INVALID_ARG = 2,     /* a value is out of range or a pointer is misaligned */
   LCV_ERR_SHAPE = 3,           /* sizes disagree (e.g. N != T*H*W) */
   LCV_ERR_LAYOUT_MISMATCH = 5, /* cond_len differs from the one the layout was built for */
-  LCV_ERR_UNSUPPORTED = 6,     /* valid but beyond what this build supports (sizes) */
+  LCV_ERR_UNSUPPORTED = 6,     /* valid but beyond what the library supports (sizes) */
   LCV_ERR_OOM = 7,             /* device allocation failed (layout build only) */
   LCV_ERR_HIP = 8              /* a HIP runtime call failed */
 } lcv_status;
