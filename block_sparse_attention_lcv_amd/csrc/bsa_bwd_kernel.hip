@@ -66,16 +66,12 @@ __device__ __forceinline__ bf16x8 fold_neg(float m, int g) {
   return g == 0 ? v : zero;
 }
 
-// The three parts of fold_neg(m) packed in 8 bytes (hi | mid << 16, lo), as the backward's
-// prep pass stores them per row, and the operand rebuilt from them (bitwise fold_neg(m, g)).
+// The three parts of fold_neg(m) packed in 8 bytes (hi | mid << 16, lo), as the backward
+// stores them per row for the fold steps of its walks.
 __device__ __forceinline__ uint2 fold_parts(float m) {
   const bf16x8 v = fold_neg(m, 0);
   const u32x4 w = __builtin_bit_cast(u32x4, v);
   return uint2{w[0], w[1]};
-}
-__device__ __forceinline__ bf16x8 fold_operand(uint2 parts, int g) {
-  const u32x4 w = {g == 0 ? parts.x : 0u, g == 0 ? parts.y : 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8, w);
 }
 
 __device__ __forceinline__ bf16x8 ones_slots(int g) {
@@ -161,15 +157,6 @@ __device__ __forceinline__ void copy_tile(const uint16_t* slice, int32_t N, int 
   const __amdgpu_buffer_rsrc_t r = uniform_rsrc((uint64_t)(uintptr_t)slice + (uint64_t)blk * kTileBytes, rows * 128);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * wave), 16, (uint32_t)(row * 128 + 16 * gch), 0,
                                            0, 0);
-}
-
-// Asynchronous copy of the 64 fp32 row values of block blk into LDS (one wavefront), zeros past
-// row N.
-__device__ __forceinline__ void copy_rows_f32(const float* slice, int32_t N, int blk, float* dst, int lane) {
-  int rows = N - 64 * blk;
-  rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
-  const __amdgpu_buffer_rsrc_t r = uniform_rsrc((uint64_t)(uintptr_t)(slice + (int64_t)64 * blk), rows * 4);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(4 * lane), 0, 0, 0);
 }
 
 // Asynchronous copy of the 64 eight-byte row values of block blk into LDS (one wavefront, two
@@ -501,33 +488,63 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
   const TrOff tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
 
-  // Q and dO (zeros past the range or the sequence), and lse and D (an empty row's there),
-  // of this wavefront's 32 rows of query block qb
+  // This walk visits every query row once, so it forms the per-row terms itself (the other
+  // backward walks take them from bwd_prep_kernel): Q' = bf16(Q log2(e)/8), lse log2(e) and
+  // D = rowsum(dO * O) of this wavefront's 32 rows of query block qb (lanes l and l ^ 32 hold
+  // 32 channels of a row each), and stores them for the key walk that runs next.  Rows past
+  // the range or the sequence read zeros and an empty row's lse.
   auto row_ok = [&](int qb, int& qq) __attribute__((always_inline)) {
     qq = 64 * qb + 32 * (wave & 1) + l32;
     return qb < blk1 && qq < P.N;
   };
-  auto load_qdo = [&](int qb, bf16x8 (&qx)[4], bf16x8 (&dx)[4]) __attribute__((always_inline)) {
+  auto issue_rows = [&](int qb, bf16x8 (&qr)[4], bf16x8 (&orw)[4], bf16x8 (&dx)[4], float& l)
+      __attribute__((always_inline)) {
     int qq;
     const bool ok = row_ok(qb, qq);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qx[ks] = load_chunk(P.qs + base * 64, qq, 2 * ks + g, ok);
+      qr[ks] = load_chunk(P.q + base * 64, qq, 2 * ks + g, ok);
+      orw[ks] = load_chunk(P.out + base * 64, qq, 2 * ks + g, ok);
       dx[ks] = load_chunk(P.dout + base * 64, qq, 2 * ks + g, ok);
     }
+    l = ok ? P.lse[base + qq] : -INFINITY;
   };
-  auto load_stats = [&](int qb, float& l2, float& d) __attribute__((always_inline)) {
+  auto finish_rows = [&](int qb, const bf16x8 (&qr)[4], const bf16x8 (&orw)[4], const bf16x8 (&dx)[4], float l,
+                         bf16x8 (&qx)[4], float& l2, float& d) __attribute__((always_inline)) {
     int qq;
     const bool ok = row_ok(qb, qq);
-    l2 = ok ? P.lse2[base + qq] : kEmptyRowLse2;
-    d = ok ? P.delta[base + qq] : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 a = __builtin_bit_cast(u32x4, orw[ks]), b = __builtin_bit_cast(u32x4, dx[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sum = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), sum);
+        sum = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), sum);
+      }
+      const u32x4 sc = scale_chunk_log2(__builtin_bit_cast(u32x4, qr[ks]));
+      qx[ks] = __builtin_bit_cast(bf16x8, sc);
+      if (ok) *reinterpret_cast<u32x4*>(P.qs + (base + qq) * 64 + 8 * (2 * ks + g)) = sc;
+    }
+    d = sum + __shfl_xor(sum, 32, 64);
+    l2 = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
+    if (ok && g == 0) {
+      P.lse2[base + qq] = l2;
+      P.delta[base + qq] = d;
+      P.fold_l[base + qq] = fold_parts(l2);
+      P.fold_d[base + qq] = fold_parts(d);
+    }
   };
 
   int qblk = blk0 + (wave >> 1);
   bf16x8 qf[4], dof[4];
   float lse2, dlt;
-  load_qdo(qblk, qf, dof);
-  load_stats(qblk, lse2, dlt);
+  {
+    bf16x8 qr[4], orw[4];
+    float l;
+    issue_rows(qblk, qr, orw, dof, l);
+    finish_rows(qblk, qr, orw, dof, l, qf, lse2, dlt);
+  }
   while (qblk < blk1) {
     const int qnext = qblk + kWaves;
 
@@ -614,10 +631,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
 
     // the next round's rows, loaded after the walk (holding them through it would spill):
     // they arrive while this round's dQ is stored and the partner wavefront computes
-    bf16x8 qf_n[4], dof_n[4];
-    float lse2_n, dlt_n;
-    load_qdo(qnext, qf_n, dof_n);
-    load_stats(qnext, lse2_n, dlt_n);
+    bf16x8 qr_n[4], or_n[4], dof_n[4];
+    float l_n;
+    issue_rows(qnext, qr_n, or_n, dof_n, l_n);
     // dQ = dQ^T / 8, rows written as 8-byte stores of 4 channels
     if (q < P.N) {
       uint16_t* row = P.dq + (base + q) * 64;
@@ -631,14 +647,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
           *reinterpret_cast<uint2*>(row + 32 * dt + 8 * R + 4 * g) = pk;
         }
     }
+    finish_rows(qnext, qr_n, or_n, dof_n, l_n, qf, lse2, dlt);
     qblk = qnext;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      qf[ks] = qf_n[ks];
-      dof[ks] = dof_n[ks];
-    }
-    lse2 = lse2_n;
-    dlt = dlt_n;
+    for (int ks = 0; ks < 4; ++ks) dof[ks] = dof_n[ks];
   }
 }
 
@@ -938,14 +950,16 @@ unsigned grid_for(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
   const bool cross = p.cross;
+  // the text-resident query walk forms the per-row terms itself
+  const bool own_prep = cross && p.q_parts > 0;
   hipError_t e = hipSuccess;
-  if (p.bh_rows > 0) {
+  if (p.bh_rows > 0 && !own_prep) {
     const int64_t threads = p.bh_rows * 8;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.q, p.out,
                        p.dout, p.lse, p.qs, p.lse2, p.delta, p.fold_l, p.fold_d, p.bh_rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-  } else if (!cross) {
+  } else if (p.bh_rows == 0 && !cross) {
     return hipSuccess;
   }
   if (!cross) {   // self-attention
