@@ -339,11 +339,12 @@ def measure_backward(bsa, torch, q, k, v, layout, w, fwd_flops: float, steps: in
     log(f"[bench] backward: {ms:.3f} ms, {eff:.1f} TFLOP/s effective (2.5x forward FLOPs), "
         f"{executed:.1f} TFLOP/s of executed matrix work")
     del out, lse, do, dq, dk, dv, ws
-    return {"bound": "mfma", "kernels": ["bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"],
+    return {"bound": "mfma", "kernels": ["bwd_dq_kernel", "bwd_dkdv_kernel"],
             "ms": round(ms, 4), "effective_flops": 2.5 * fwd_flops, "achieved": round(eff, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / MFMA_BF16_PEAK_TFLOPS, 4),
             "executed_tflops": round(executed, 3), "launches": steps,
-            "what": "dQ, dK, dV of the block-sparse attention (D = rowsum(dO*O) pass, query walk, key walk)"}
+            "what": "dQ, dK, dV of the block-sparse attention (query walk with the per-row D = rowsum(dO*O), "
+                    "key walk)"}
 
 
 def measure_cross(bsa, torch, q, w, steps: int, stream, with_backward: bool = True):
@@ -392,7 +393,7 @@ def measure_cross(bsa, torch, q, w, steps: int, stream, with_backward: bool = Tr
     log(f"[bench] cross-attention backward: {bms:.4f} ms, {eff:.1f} TFLOP/s effective (2.5x forward FLOPs), "
         f"{executed:.1f} TFLOP/s of executed matrix work")
     del k, v, out, lse, do, dq, dk, dv, ws
-    bwd = {"bound": "mfma", "kernels": ["bwd_prep_kernel", "bwd_dq_kernel<cross>", "bwd_dkdv_kernel<cross>",
+    bwd = {"bound": "mfma", "kernels": ["bwd_dq_cross_resident_kernel", "bwd_dkdv_kernel<cross>",
                                         "bwd_cross_reduce_kernel"],
            "ms": round(bms, 4), "effective_flops": 2.5 * flops, "achieved": round(eff, 3),
            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / MFMA_BF16_PEAK_TFLOPS, 4),

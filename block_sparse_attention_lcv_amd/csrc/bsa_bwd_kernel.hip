@@ -11,11 +11,11 @@
 // forward's probability of the pair (up to the order of the fp32 additions) and agrees with
 // the forward's LSE however large the scores.  With S' = Q' K^T the forward's score in log2
 // units, dS/dK = Q' ln 2 (the derivative of that score in natural units) and dS/dQ = K / 8.
-// Three kernels:
-//  * bwd_prep_kernel: D = rowsum(dO * O), lse * log2(e) and Q' per row (HBM-bound, one pass
-//    over Q, O and dO) into the workspace;
+// Two kernels:
 //  * bwd_dq_kernel: the row walk of the forward -- a workgroup of 8 wavefronts owns 4 query
 //    blocks (32 rows per wavefront) and streams the K and V blocks of their rows through LDS;
+//    it first forms its rows' D = rowsum(dO * O), lse * log2(e) and Q' (row_terms) and
+//    stores them in the workspace for the key walk;
 //    per 32-key half it forms S^T - lse * log2(e) = K Q'^T and dP^T - D = V dO^T with
 //    v_mfma_f32_32x32x16_bf16 (the row's lse and D are folded into one extra MFMA step each),
 //    then dS^T = exp2(.) (dP^T - D) and dQ^T += K^T dS^T with K^T read through
@@ -170,36 +170,35 @@ __device__ __forceinline__ void copy_rows_u64(const uint2* slice, int32_t N, int
                                            (uint32_t)(256 + 4 * lane), 0, 0, 0);
 }
 
-// D = rowsum(dO * O), lse * log2(e) and Q' = bf16(Q * log2(e)/8) per row, and the key walk's
-// fold operands of -lse * log2(e) and -D (their three bf16 parts); one thread per 8-channel
-// chunk of a row.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* q, const uint16_t* out, const uint16_t* dout,
-                                                       const float* lse, uint16_t* qs, float* lse2, float* delta,
-                                                       uint2* fold_l, uint2* fold_d, int64_t rows) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid >> 3;
-  const int c = (int)(gid & 7);
-  if (row >= rows) return;   // the eight lanes of a row leave together
-  const u32x4 qc = *reinterpret_cast<const u32x4*>(q + row * 64 + 8 * c);
-  const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * 64 + 8 * c);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * 64 + 8 * c);
-  *reinterpret_cast<u32x4*>(qs + row * 64 + 8 * c) = scale_chunk_log2(qc);
-  float s = 0.f;
+// The per-row terms of the backward, formed by the query walks (which visit every query row
+// once) and stored for the key walk that runs after them: Q' = bf16(Q log2(e)/8) (the
+// forward's query operand), lse log2(e) (an empty row's value for lse = -inf) and
+// D = rowsum(dO * O), with the fold parts of -lse log2(e) and -D.  The lane holds channel
+// chunks 2ks + g (ks = 0..3) of row `row` in qr, orw (O) and dx (dO), the partner lane l ^ 32
+// the other four; ok: the row exists (else nothing is stored).  Returns Q' in qx.
+__device__ __forceinline__ void row_terms(const BwdParams& P, int64_t row, bool ok, int g, const bf16x8 (&qr)[4],
+                                          const bf16x8 (&orw)[4], const bf16x8 (&dx)[4], float l, bf16x8 (&qx)[4],
+                                          float& l2, float& d) {
+  float sum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    s = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), s);
-    s = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), s);
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 a = __builtin_bit_cast(u32x4, orw[ks]), b = __builtin_bit_cast(u32x4, dx[ks]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), sum);
+      sum = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), sum);
+    }
+    const u32x4 sc = scale_chunk_log2(__builtin_bit_cast(u32x4, qr[ks]));
+    qx[ks] = __builtin_bit_cast(bf16x8, sc);
+    if (ok) *reinterpret_cast<u32x4*>(P.qs + row * 64 + 8 * (2 * ks + g)) = sc;
   }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
-  if (c == 0) {
-    delta[row] = s;
-    const float l = lse[row];
-    const float l2 = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
-    lse2[row] = l2;
-    fold_l[row] = fold_parts(l2);
-    fold_d[row] = fold_parts(s);
+  d = sum + __shfl_xor(sum, 32, 64);
+  l2 = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
+  if (ok && g == 0) {
+    P.lse2[row] = l2;
+    P.delta[row] = d;
+    P.fold_l[row] = fold_parts(l2);
+    P.fold_d[row] = fold_parts(d);
   }
 }
 
@@ -259,16 +258,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
   const bool wave_on = qblk < P.n_blocks;
   const int q = 64 * qblk + 32 * (wave & 1) + l32;
   const bool qok = wave_on && q < P.N;
+  // the row's terms (row_terms: Q', and lse in log2 units and D, which are folded into the
+  // S^T and dP^T accumulators by one extra MFMA step each), stored for the key walk
   bf16x8 qf[4], dof[4];
+  float lse2, dlt;
+  {
+    bf16x8 qr[4], orw[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    qf[ks] = load_chunk(P.qs + base * 64, q, 2 * ks + g, qok);
-    dof[ks] = load_chunk(P.dout + base * 64, q, 2 * ks + g, qok);
+    for (int ks = 0; ks < 4; ++ks) {
+      qr[ks] = load_chunk(P.q + base * 64, q, 2 * ks + g, qok);
+      orw[ks] = load_chunk(P.out + base * 64, q, 2 * ks + g, qok);
+      dof[ks] = load_chunk(P.dout + base * 64, q, 2 * ks + g, qok);
+    }
+    const float l = qok ? P.lse[base + q] : -INFINITY;
+    row_terms(P, base + q, qok, g, qr, orw, dof, l, qf, lse2, dlt);
   }
-  // the row's lse (log2 units) and D are folded into the S^T and dP^T accumulators by one
-  // extra MFMA step each
-  const float lse2 = qok ? P.lse2[base + q] : kEmptyRowLse2;
-  const float dlt = qok ? P.delta[base + q] : 0.f;
   const bf16x8 fold_l = fold_neg(lse2, g);
   const bf16x8 fold_d = fold_neg(dlt, g);
   const int key_end = key_end_of<CROSS>(P, bh);                 // keys [0, key_end) exist
@@ -488,10 +492,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
   const TrOff tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
 
-  // This walk visits every query row once, so it forms the per-row terms itself (the other
-  // backward walks take them from bwd_prep_kernel): Q' = bf16(Q log2(e)/8), lse log2(e) and
-  // D = rowsum(dO * O) of this wavefront's 32 rows of query block qb (lanes l and l ^ 32 hold
-  // 32 channels of a row each), and stores them for the key walk that runs next.  Rows past
+  // The per-row terms (row_terms) of this wavefront's 32 rows of query block qb; rows past
   // the range or the sequence read zeros and an empty row's lse.
   auto row_ok = [&](int qb, int& qq) __attribute__((always_inline)) {
     qq = 64 * qb + 32 * (wave & 1) + l32;
@@ -513,27 +514,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
                          bf16x8 (&qx)[4], float& l2, float& d) __attribute__((always_inline)) {
     int qq;
     const bool ok = row_ok(qb, qq);
-    float sum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 a = __builtin_bit_cast(u32x4, orw[ks]), b = __builtin_bit_cast(u32x4, dx[ks]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sum = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), sum);
-        sum = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), sum);
-      }
-      const u32x4 sc = scale_chunk_log2(__builtin_bit_cast(u32x4, qr[ks]));
-      qx[ks] = __builtin_bit_cast(bf16x8, sc);
-      if (ok) *reinterpret_cast<u32x4*>(P.qs + (base + qq) * 64 + 8 * (2 * ks + g)) = sc;
-    }
-    d = sum + __shfl_xor(sum, 32, 64);
-    l2 = (l == -INFINITY) ? kEmptyRowLse2 : l * kLog2e;
-    if (ok && g == 0) {
-      P.lse2[base + qq] = l2;
-      P.delta[base + qq] = d;
-      P.fold_l[base + qq] = fold_parts(l2);
-      P.fold_d[base + qq] = fold_parts(d);
-    }
+    row_terms(P, base + qq, ok, g, qr, orw, dx, l, qx, l2, d);
   };
 
   int qblk = blk0 + (wave >> 1);
@@ -950,18 +931,9 @@ unsigned grid_for(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 
 hipError_t launch_bsa_bwd(const BwdParams& p, hipStream_t stream) {
   const bool cross = p.cross;
-  // the text-resident query walk forms the per-row terms itself
-  const bool own_prep = cross && p.q_parts > 0;
   hipError_t e = hipSuccess;
-  if (p.bh_rows > 0 && !own_prep) {
-    const int64_t threads = p.bh_rows * 8;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p.q, p.out,
-                       p.dout, p.lse, p.qs, p.lse2, p.delta, p.fold_l, p.fold_d, p.bh_rows);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  } else if (p.bh_rows == 0 && !cross) {
-    return hipSuccess;
-  }
+  // the query walks form the per-row terms (row_terms) that the key walk reads
+  if (p.bh_rows == 0 && !cross) return hipSuccess;
   if (!cross) {   // self-attention
     hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(grid_for((int64_t)p.bh * p.n_st)), dim3(kBwdThreads), 0, stream, p);
     e = hipGetLastError();
