@@ -645,8 +645,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
     // interleaved with the first half's softmax, so that where the two wavefronts of a SIMD
     // compete for issue this segment goes first (about 1% less time per launch at 720p;
     // raised over both interleaved segments it gained less, around the matrix-only runs of
-    // the block it took longer).
-    __builtin_amdgcn_s_setprio(1);
+    // the block it took longer).  The variants that rotate K in the kernel keep the normal
+    // priority: with their K staging through registers it cost 0.5%.
+    if constexpr (!ROPE_K) __builtin_amdgcn_s_setprio(1);
     if (masked) mask_half(key0, 0, s0);
     rebase(s0);
     qk_half(ka1, s1);
@@ -660,7 +661,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
     if (__builtin_expect(__any(trig[0] || trig[1]), 0)) softmax_slow(s0, p0, psum, trig, delta);
     lsum[0] += psum[0];
     lsum[1] += psum[1];
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!ROPE_K) __builtin_amdgcn_s_setprio(0);
     if (masked) mask_half(key0, 1, s1);
     rebase(s1);
     pv_half(vb, 0, p0);
