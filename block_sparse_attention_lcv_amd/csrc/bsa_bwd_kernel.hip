@@ -455,13 +455,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
 // ------------------------------------------------------------ dQ of the cross-attention
 // With at most kCrossResidentBlocks text blocks (512 tokens) a head's text K and V fit in
 // LDS (128 KB): each workgroup loads them once and streams a range of query blocks past
-// them, four per round (two wavefronts per query block, 32 rows each, as in bwd_dq_kernel).
+// them in units of 32 query rows (two per query block, as in bwd_dq_kernel), handed out to
+// the wavefronts one at a time.
 // The walk has no copies and no barriers, so the wavefronts run on their own; each loads its
-// next round's Q, dO, lse and D right after its walk, under its dQ stores and the partner
+// next unit's Q, dO, lse and D right after its walk, under its dQ stores and the partner
 // wavefront's work.  Per text block the arithmetic is bwd_dq_kernel's (no condition rule).
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(const BwdParams P) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[kCrossResidentBlocks * kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v[kCrossResidentBlocks * kTileBytes];
+  __shared__ int next_unit;   // the next unit of the range not yet handed out
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -484,6 +486,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     copy_tile(P.k + kv_base * 64, key_end, j, lds_k + j * kTileBytes, wave, lane);
     copy_tile(P.v + kv_base * 64, key_end, j, lds_v + j * kTileBytes, wave, lane);
   }
+  if (tid == 0) next_unit = kBwdThreads / 64;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -492,16 +495,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
   for (int ks = 0; ks < 4; ++ks) ka_off[ks] = tile_off(l32, 2 * ks + g);
   const TrOff tr0 = tr_off(lane, 0), tr1 = tr_off(lane, 1);
 
-  // The per-row terms (row_terms) of this wavefront's 32 rows of query block qb; rows past
-  // the range or the sequence read zeros and an empty row's lse.
-  auto row_ok = [&](int qb, int& qq) __attribute__((always_inline)) {
-    qq = 64 * qb + 32 * (wave & 1) + l32;
+  // The range's work is handed out in units of 32 query rows: unit u is half u & 1 of query
+  // block blk0 + u / 2.  Wavefront w starts on unit w and then takes the next unit not yet
+  // handed out: the two wavefronts of a SIMD do not progress alike (the older one issues
+  // first), and with fixed shares the faster one would finish early and leave its SIMD to the
+  // other alone.  A unit's results do not depend on which wavefront computes it.
+  // The per-row terms (row_terms) of the 32 rows of unit u; rows past the range or the
+  // sequence read zeros and an empty row's lse.
+  auto row_ok = [&](int u, int& qq) __attribute__((always_inline)) {
+    const int qb = blk0 + (u >> 1);
+    qq = 64 * qb + 32 * (u & 1) + l32;
     return qb < blk1 && qq < P.N;
   };
-  auto issue_rows = [&](int qb, bf16x8 (&qr)[4], bf16x8 (&orw)[4], bf16x8 (&dx)[4], float& l)
+  auto issue_rows = [&](int u, bf16x8 (&qr)[4], bf16x8 (&orw)[4], bf16x8 (&dx)[4], float& l)
       __attribute__((always_inline)) {
     int qq;
-    const bool ok = row_ok(qb, qq);
+    const bool ok = row_ok(u, qq);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       qr[ks] = load_chunk(P.q + base * 64, qq, 2 * ks + g, ok);
@@ -510,26 +519,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     }
     l = ok ? P.lse[base + qq] : -INFINITY;
   };
-  auto finish_rows = [&](int qb, const bf16x8 (&qr)[4], const bf16x8 (&orw)[4], const bf16x8 (&dx)[4], float l,
+  auto finish_rows = [&](int u, const bf16x8 (&qr)[4], const bf16x8 (&orw)[4], const bf16x8 (&dx)[4], float l,
                          bf16x8 (&qx)[4], float& l2, float& d) __attribute__((always_inline)) {
     int qq;
-    const bool ok = row_ok(qb, qq);
+    const bool ok = row_ok(u, qq);
     row_terms(P, base + qq, ok, g, qr, orw, dx, l, qx, l2, d);
   };
 
-  int qblk = blk0 + (wave >> 1);
+  int unit = wave;
   bf16x8 qf[4], dof[4];
   float lse2, dlt;
   {
     bf16x8 qr[4], orw[4];
     float l;
-    issue_rows(qblk, qr, orw, dof, l);
-    finish_rows(qblk, qr, orw, dof, l, qf, lse2, dlt);
+    issue_rows(unit, qr, orw, dof, l);
+    finish_rows(unit, qr, orw, dof, l, qf, lse2, dlt);
   }
-  while (qblk < blk1) {
-    const int qnext = qblk + kWaves;
+  while (blk0 + (unit >> 1) < blk1) {
+    int taken = 0;
+    if (lane == 0) taken = atomicAdd(&next_unit, 1);
+    const int unext = __builtin_amdgcn_readfirstlane(taken);
 
-    const int q = 64 * qblk + 32 * (wave & 1) + l32;
+    const int q = 64 * (blk0 + (unit >> 1)) + 32 * (unit & 1) + l32;
     const uint2 fold_l = fold_parts(lse2);
     const uint2 fold_d = fold_parts(dlt);
     f32x16 dqt[2];
@@ -614,7 +625,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
     // they arrive while this round's dQ is stored and the partner wavefront computes
     bf16x8 qr_n[4], or_n[4], dof_n[4];
     float l_n;
-    issue_rows(qnext, qr_n, or_n, dof_n, l_n);
+    issue_rows(unext, qr_n, or_n, dof_n, l_n);
     // dQ = dQ^T / 8, rows written as 8-byte stores of 4 channels
     if (q < P.N) {
       uint16_t* row = P.dq + (base + q) * 64;
@@ -628,8 +639,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_cross_resident_kernel(c
           *reinterpret_cast<uint2*>(row + 32 * dt + 8 * R + 4 * g) = pk;
         }
     }
-    finish_rows(qnext, qr_n, or_n, dof_n, l_n, qf, lse2, dlt);
-    qblk = qnext;
+    finish_rows(unext, qr_n, or_n, dof_n, l_n, qf, lse2, dlt);
+    unit = unext;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) dof[ks] = dof_n[ks];
   }

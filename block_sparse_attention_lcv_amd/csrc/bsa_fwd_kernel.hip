@@ -504,6 +504,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
   if constexpr (ROPE_K) {
     if (cnt > 0) stage_store_k(P, lds_k0, ent_cur >> 8, wave, lane, tab, kreg);
   }
+  // the resident walk's counter of handed-out query blocks (in the otherwise unused 16 bytes of
+  // lds_k1): every wavefront starts on its own block, the next ones are taken from here
+  int* const next_block = reinterpret_cast<int*>(lds_k1);
+  if constexpr (RESIDENT) {
+    if (tid == 0) *next_block = level * P.q_per_part + 2 * kWaves;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -741,8 +747,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
   };
 
   if constexpr (RESIDENT) {
-    // query blocks [blk0, blk1) of the head, wavefront w taking blk0 + w, blk0 + w + 2 kWaves,
-    // ...; the next block's rows are loaded before this block's output is stored
+    // query blocks [blk0, blk1) of the head: wavefront w starts on blk0 + w and then takes the
+    // next block not yet handed out.  The two wavefronts of a SIMD do not progress alike (the
+    // older one issues first), so with fixed shares the faster one finished about 15% earlier
+    // and left its SIMD to the other alone.  A block's result does not depend on which
+    // wavefront computes it.  The next block's rows are loaded before this block's output is
+    // stored.
     const int blk0 = level * P.q_per_part;
     const int blk1 = blk0 + P.q_per_part < P.n_blocks ? blk0 + P.q_per_part : P.n_blocks;
     int qb = blk0 + wave;
@@ -757,7 +767,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams& P) {
         shift_offsets(2 * kTileBytes);
       }
       shift_offsets(-2 * kTileBytes * cnt);
-      const int qn = qb + 2 * kWaves;
+      int taken = 0;
+      if (lane == 0) taken = atomicAdd(next_block, 1);
+      const int qn = __builtin_amdgcn_readfirstlane(taken);
       if (qn < blk1) load_query(qn);
       store_output();
       clear_state();

@@ -267,11 +267,12 @@ CrossBwdPlan cross_bwd_plan(int64_t bh, int32_t n_q, int32_t kv_len) {
     chunks = (pl.n_q_blocks + pl.q_chunk - 1) / pl.q_chunk;   // no empty chunk
   }
   pl.n_chunks = (int32_t)chunks;
-  // query walk: with the text in LDS, about 512 workgroups of whole rounds of 4 query blocks
+  // query walk: with the text in LDS, about 512 workgroups, each a range of query blocks as
+  // equal as whole blocks allow (its wavefronts share it 32 rows at a time), at least 4 long
   if (pl.n_q_blocks > 0 && pl.n_kv_blocks <= lcv::kCrossResidentBlocks) {
     int64_t parts = (LCV_CROSS_QUERY_WALK_WORKGROUPS + bh - 1) / bh;
     parts = parts < pl.n_st ? parts : pl.n_st;
-    const int64_t per = ((pl.n_q_blocks + parts - 1) / parts + lcv::kWaves - 1) / lcv::kWaves * lcv::kWaves;
+    const int64_t per = (pl.n_q_blocks + parts - 1) / parts;
     pl.q_per_part = (int32_t)per;
     pl.q_parts = (int32_t)((pl.n_q_blocks + per - 1) / per);
   }
@@ -577,13 +578,15 @@ lcv_status lcv_cross_attention(const void* q, const void* k, const void* v, int3
   p.heads = heads;
   // With at most kCrossResidentBlocks text blocks the text stays in LDS: about
   // LCV_CROSS_FWD_WORKGROUPS workgroups (one per compute unit), each streaming a range of
-  // query blocks (a multiple of its 2 * kWaves wavefronts) past its head's text.
+  // query blocks past its head's text.  The ranges of a head are as equal as whole blocks
+  // allow (the wavefronts of a workgroup share its range block by block), and at least as
+  // long as the workgroup has wavefronts.
   if ((int64_t)kv_len <= (int64_t)lcv::kCrossResidentBlocks * 64) {
     constexpr int64_t kRound = 2 * lcv::kWaves;
     const int64_t rounds = (n_blocks + kRound - 1) / kRound;
     int64_t parts = (LCV_CROSS_FWD_WORKGROUPS + bh - 1) / bh;
     parts = parts < rounds ? parts : rounds;
-    const int64_t per = ((n_blocks + parts - 1) / parts + kRound - 1) / kRound * kRound;
+    const int64_t per = (n_blocks + parts - 1) / parts;
     parts = (n_blocks + per - 1) / per;
     p.q_per_part = (int32_t)per;
     p.n_st_active = (int32_t)parts;
