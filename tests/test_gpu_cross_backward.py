@@ -75,6 +75,10 @@ CASES = [
     ("many-chunks", 1, 2, 4097, 300, [7]),        # 33 query chunks of 2 blocks, last one ragged
     ("empty-text-item", 2, 2, 130, 96, [0, 96]),
     ("lens-clamped", 2, 1, 70, 40, [-3, 99]),
+    # 256 (batch, head) pairs: one query range per head, 20 query blocks for the forward's 8
+    # wavefronts and 20 units of 32 rows for the backward query walk's, handed out by the
+    # workgroup's counter
+    ("many-heads-long-ranges", 2, 128, 1221, 150, [150, 61]),
     ("no-query", 2, 2, 0, 100, [100, 30]),         # dk = dv = 0
     ("no-text", 1, 2, 100, 0, None),               # dq = 0
 ]
