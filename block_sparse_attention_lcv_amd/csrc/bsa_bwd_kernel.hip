@@ -374,6 +374,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
     sdp_half(kb, vb, 0, s0, dp0);
     if (__builtin_expect(masked, 0)) mask_half(j, 0, s0);
     copies();
+    // issue priority raised over the interleaved segment, as in the forward
+    __builtin_amdgcn_s_setprio(1);
     sdp_half(kb, vb, 1, s1, dp1);
     ds_half(s0, dp0, d0);
     // 8 K/V reads, then the second half's 10 MFMAs each followed by vector work of the first
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdParams 
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (__builtin_expect(masked, 0)) mask_half(j, 1, s1);
     dq_half(kb, 0, d0);
     ds_half(s1, dp1, d1);
@@ -802,6 +805,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
     sdp_half(qb, ob, lb, db, 0, s0, dp0);
     if (__builtin_expect(masked, 0)) mask_half(i, 0, s0);
     copies();
+    __builtin_amdgcn_s_setprio(1);
     sdp_half(qb, ob, lb, db, 1, s1, dp1);
     pds_half(s0, dp0, p0, d0);
     __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
@@ -810,6 +814,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdParam
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (__builtin_expect(masked, 0)) mask_half(i, 1, s1);
     upd_half(qb, ob, 0, p0, d0);
     pds_half(s1, dp1, p1, d1);
